@@ -1,0 +1,156 @@
+"""Host block manager: allocation, sharing and copy-on-write (oracle; test infrastructure).
+
+What it follows:
+
+* Blocks hold a fixed number of tokens ("PagedAttention Explained", "How
+  PagedAttention works", step 1).  A sequence of ``L`` tokens owns
+  ``ceil(L / block_size)`` blocks, every one full except possibly the last
+  (step 2; and "What does PagedAttention change in LLM KV allocation?",
+  "Calculate unused block space", whose 35-token example needs three
+  16-token blocks and leaves thirteen slots of the last one empty).
+* A new physical block is taken only when the sequence's last block is full;
+  nothing is reserved ahead (step 4).  Blocks go back to the pool when the
+  request finishes (third page, same section).
+* The per-sequence block table maps logical to physical blocks, in any order
+  (step 3).  ``free_order`` sets the order in which the pool hands out ids,
+  which is how a caller produces scattered placements.
+* Several tables may point at one physical block; each block carries a
+  reference count.  A sequence about to write into a block whose count is
+  above one first gets its own copy, and its table is pointed at the copy
+  ("Sharing blocks between sequences").  Reading: the writer copies while the
+  count is above one and decrements it, so the last holder writes in place;
+  ``append`` reports each copy as a ``(src, dst)`` pair for a block-copy call.
+* The only waste of a sequence is the unused tail of its last block, less than
+  one block ("How PagedAttention works", closing paragraph, and the table
+  "Contiguous allocation vs PagedAttention").
+"""
+
+from collections import deque
+
+import numpy as np
+
+
+class OutOfBlocks(RuntimeError):
+    """The pool has no free block left."""
+
+
+def blocks_for(length, block_size):
+    """Number of blocks a sequence of ``length`` tokens occupies."""
+    if length < 0 or block_size <= 0:
+        raise ValueError("length must be >= 0 and block_size > 0")
+    return -(-length // block_size)
+
+
+def tail_waste(length, block_size):
+    """Unused slots in a sequence's blocks (all in its last block)."""
+    return blocks_for(length, block_size) * block_size - length
+
+
+class BlockManager:
+    """Pool of ``num_blocks`` physical blocks of ``block_size`` token slots."""
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of the pool ids")
+        self.free = deque(order)
+        self.refcount = [0] * num_blocks
+        self.fill = [0] * num_blocks
+        self.tables = {}
+        self.lengths = {}
+
+    # -- pool -------------------------------------------------------------
+    def _take(self):
+        if not self.free:
+            raise OutOfBlocks("no free block in the pool")
+        b = self.free.popleft()
+        self.refcount[b] = 1
+        self.fill[b] = 0
+        return b
+
+    def _drop(self, b):
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self.fill[b] = 0
+            self.free.append(b)
+
+    # -- sequences ----------------------------------------------------------
+    def add(self, seq):
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq!r} exists")
+        self.tables[seq] = []
+        self.lengths[seq] = 0
+
+    def append(self, seq, n=1):
+        """Store ``n`` new tokens of ``seq``.
+
+        Returns ``(slots, copies)``: the slot of each new token
+        (``physical * block_size + offset``) and the ``(src, dst)`` block
+        copies the writes require, in order.
+        """
+        BS = self.block_size
+        table = self.tables[seq]
+        slots, copies = [], []
+        for _ in range(n):
+            t = self.lengths[seq]
+            offset = t % BS
+            if offset == 0:
+                b = self._take()
+                table.append(b)
+            else:
+                b = table[-1]
+                if self.refcount[b] > 1:
+                    nb = self._take()
+                    copies.append((b, nb))
+                    self.fill[nb] = self.fill[b]
+                    self.refcount[b] -= 1
+                    table[-1] = nb
+                    b = nb
+            slots.append(b * BS + offset)
+            self.fill[b] = max(self.fill[b], offset + 1)
+            self.lengths[seq] = t + 1
+        return slots, copies
+
+    def fork(self, parent, child):
+        """``child`` starts as a copy of ``parent`` that shares all its blocks."""
+        self.add(child)
+        self.tables[child] = list(self.tables[parent])
+        self.lengths[child] = self.lengths[parent]
+        for b in self.tables[child]:
+            self.refcount[b] += 1
+
+    def free_sequence(self, seq):
+        """Release ``seq``; blocks nobody else references return to the pool."""
+        for b in self.tables.pop(seq):
+            self._drop(b)
+        del self.lengths[seq]
+
+    # -- views --------------------------------------------------------------
+    def table_array(self, seqs, width):
+        """int32 ``[len(seqs), width]`` block table, unused entries ``-1``."""
+        out = np.full((len(seqs), width), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            row = self.tables[s]
+            if len(row) > width:
+                raise ValueError(f"sequence {s!r} needs {len(row)} table entries > {width}")
+            out[i, : len(row)] = row
+        return out
+
+    def stats(self):
+        """Allocation figures of the pool (the measurements the third page lists)."""
+        allocated = [b for b in range(self.num_blocks) if self.refcount[b] > 0]
+        used = sum(self.fill[b] for b in allocated)
+        slots = len(allocated) * self.block_size
+        return {
+            "allocated_blocks": len(allocated),
+            "allocated_slots": slots,
+            "used_slots": used,
+            "unused_slots": slots - used,
+            "waste_fraction": (slots - used) / slots if slots else 0.0,
+            "free_blocks": len(self.free),
+            "sequences": len(self.tables),
+        }

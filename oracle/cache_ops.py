@@ -1,0 +1,63 @@
+"""Slot write and block copy, bitwise (oracle; test infrastructure).
+
+* Slot write: each new token's key and value rows (``[kv_heads, head_dim]``)
+  go to the slot the caller assigned, i.e. physical block ``slot //
+  block_size`` at offset ``slot % block_size`` ("PagedAttention Explained",
+  "The problem: the KV cache is big and unpredictable": the cache grows by one
+  entry per new token; "How PagedAttention works", steps 2-4 for where it
+  lands).  Reading: ``slot = physical_block * block_size + offset``; a
+  negative slot means "no write" (padding).  Duplicate slots within one call
+  are outside the contract.
+* Block copy: before a sequence writes into a block that other sequences
+  still reference, the block is copied and the writer's table is pointed at
+  the copy (same page, "Sharing blocks between sequences").  Here the copy
+  itself: for every ``(src, dst)`` pair, the whole ``dst`` block of both caches
+  becomes the pre-call ``src`` block.  Reading: within one call the ``dst`` ids
+  are distinct and none equals any ``src``, so the order of pairs does not
+  matter.
+
+Both operate on raw stored values (float32 or uint16 bit patterns) and never
+round or convert anything.
+"""
+
+import numpy as np
+
+
+def kv_write(k_cache, v_cache, k, v, slot_mapping, inplace=False):
+    """Write token rows into their slots.  Returns the (new) caches.
+
+    ``k``/``v`` are ``[T, kv_heads, head_dim]``; ``slot_mapping`` is ``[T]``.
+    """
+    if not inplace:
+        k_cache = k_cache.copy()
+        v_cache = v_cache.copy()
+    num_blocks, block_size = k_cache.shape[:2]
+    for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, block_size)
+        if block >= num_blocks:
+            raise IndexError(f"slot {slot} is outside the pool")
+        k_cache[block, offset] = k[i]
+        v_cache[block, offset] = v[i]
+    return k_cache, v_cache
+
+
+def block_copy(k_cache, v_cache, pairs, inplace=False):
+    """Copy whole physical blocks ``src -> dst`` in both caches.
+
+    ``pairs`` is ``[n, 2]`` of ``(src, dst)``.  Sources are read from the
+    state before the call.
+    """
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    src, dst = pairs[:, 0], pairs[:, 1]
+    if len(set(dst.tolist())) != len(dst) or set(dst.tolist()) & set(src.tolist()):
+        raise ValueError("block copy pairs need distinct dst ids, none equal to a src id")
+    k_src = k_cache[src].copy()
+    v_src = v_cache[src].copy()
+    if not inplace:
+        k_cache = k_cache.copy()
+        v_cache = v_cache.copy()
+    k_cache[dst] = k_src
+    v_cache[dst] = v_src
+    return k_cache, v_cache

@@ -1,0 +1,90 @@
+"""The seeded input generator: determinism and structure of the layouts."""
+
+import numpy as np
+import pytest
+
+from workloads import CONFIGS, build_layout, cow_layout, generate_host, get_config, \
+    f32_to_bf16_bits, decode_slots
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], np.float32)
+    bits = f32_to_bf16_bits(x)
+    # 1+2^-8 is a tie between 1 and 1+2^-7: even mantissa (1.0) wins;
+    # 1+3*2^-8 is a tie between 1+2^-7 and 1+2^-6: even (1+2^-6) wins
+    assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F80]
+
+
+def test_host_generation_is_deterministic():
+    cfg = get_config("c1_tiny_f32")
+    a, b = generate_host(cfg), generate_host(cfg)
+    for name in ("q", "k_cache", "v_cache", "new_k", "new_v", "slot_mapping", "block_table"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_c1_layout():
+    cfg = get_config("c1_tiny_f32")
+    lay = build_layout(cfg)
+    assert list(lay.seq_lens) == [35, 16, 1, 100]
+    assert lay.num_blocks == 32 and lay.used_blocks == 12
+    used = lay.block_table[lay.block_table >= 0]
+    assert len(set(used.tolist())) == 12
+    assert [int((row >= 0).sum()) for row in lay.block_table] == [3, 1, 1, 7]
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_layout_structure(name):
+    cfg = CONFIGS[name]
+    lay = build_layout(cfg)
+    BS = cfg.block_size
+    S = cfg.num_seqs
+    assert lay.seq_lens.shape == (S,)
+    lo, hi = cfg.len_range
+    if not cfg.seq_lens:
+        assert lay.seq_lens.min() >= lo + cfg.prefix_tokens
+        assert lay.seq_lens.max() <= hi + cfg.prefix_tokens
+    nblk = -(-lay.seq_lens.astype(np.int64) // BS)
+    assert np.array_equal((lay.block_table >= 0).sum(1), nblk)
+    for s in range(S):
+        row = lay.block_table[s]
+        assert np.all(row[: nblk[s]] >= 0) and np.all(row[nblk[s]:] == -1)
+    # every referenced id is in the pool; private ids appear once
+    used = lay.block_table[lay.block_table >= 0].astype(np.int64)
+    assert used.min() >= 0 and used.max() < lay.num_blocks
+    shared = set(lay.shared_blocks.tolist())
+    private = [b for b in used.tolist() if b not in shared]
+    assert len(private) == len(set(private))
+    assert set(lay.spare_blocks.tolist()).isdisjoint(used.tolist())
+    assert lay.used_blocks + lay.spare_blocks.size == lay.num_blocks
+    if cfg.pool_blocks == 0:
+        assert lay.num_blocks == int(np.ceil(cfg.pool_factor * lay.used_blocks))
+
+
+def test_c4_shared_prefix_structure():
+    cfg = get_config("c4_prefix_bf16")
+    lay = build_layout(cfg)
+    assert lay.shared_blocks.size == 64
+    assert np.all(lay.block_table[:, :64] == lay.shared_blocks[None, :])
+    counts = np.bincount(lay.block_table[lay.block_table >= 0], minlength=lay.num_blocks)
+    assert np.all(counts[lay.shared_blocks] == 128)
+
+
+def test_decode_slots_are_last_positions():
+    cfg = get_config("c1_tiny_f32")
+    lay = build_layout(cfg)
+    slots = decode_slots(lay.block_table, lay.seq_lens, cfg.block_size)
+    for s, L in enumerate(lay.seq_lens):
+        t = L - 1
+        assert slots[s] == lay.block_table[s, t // 16] * 16 + t % 16
+    assert decode_slots(lay.block_table, np.array([0, 1, 1, 1]), 16)[0] == -1
+
+
+def test_cow_layout_pairs_and_tables():
+    lay = build_layout(get_config("c4_prefix_bf16"))
+    sc = cow_layout(lay, 1016)
+    assert sc["pairs"].shape == (127, 2)
+    assert np.all(sc["pairs"][:, 0] == lay.shared_blocks[63])
+    assert len(set(sc["pairs"][:, 1].tolist())) == 127
+    assert np.all(sc["table_after"][127] == sc["table_before"][127])
+    assert np.all(sc["table_after"][:127, 63] == sc["pairs"][:, 1])
+    assert np.all(sc["write_slots"] % 16 == 8)
