@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV-cache path on one MI355X.
+
+One step = ``paged_kv_write`` of every sequence's new token, then
+``paged_attn_decode`` over the whole batch, both on the current stream, with
+every input already resident in HBM.  The default workload is the bf16 GQA
+4k-context batch (256 sequences, lengths U{3072..4096}, 32 query / 8 KV heads,
+head dim 128, block 16), drawn on the device from its seed.
+
+Prints one JSON line.  ``value`` is the step's effective KV throughput: the
+algorithmic bytes of one step (every cached K/V byte the batch attends to
+read once, q and out, the tables, the new rows written) divided by the
+wall-clock time per step.  ``roofline`` reports the decode launch alone,
+timed with events recorded on the launch stream around it in every timed step.
+``cpu_baseline`` times the fp64 oracle on the host on a bounded sample of the
+same batch.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: effective KV GB/s (% HBM peak) + seqs/sec, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "c3_gqa4k_bf16"
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--part-tokens", type=int, default=None,
+                   help="split-K partition length (default: the workload's, else the library's)")
+    p.add_argument("--cpu-sample", type=int, default=128,
+                   help="sequences the oracle computes for the CPU baseline (0 skips it)")
+    return p.parse_args(argv)
+
+
+def step_bytes(cfg, lens):
+    """Algorithmic bytes of one decode launch and of one slot-write launch."""
+    import numpy as np
+    e = cfg.elem_bytes
+    lens = np.asarray(lens, dtype=np.int64)
+    blocks = -(-lens // cfg.block_size)
+    kv = int(lens.sum()) * cfg.kv_heads * cfg.head_dim * e * 2
+    qo = cfg.num_seqs * cfg.q_heads * cfg.head_dim * e * 2
+    tables = int(blocks.sum()) * 4 + cfg.num_seqs * 4
+    decode = kv + qo + tables
+    write = cfg.num_seqs * (cfg.kv_heads * cfg.head_dim * e * 2 * 2 + 8)
+    return {"decode": decode, "kv_read": kv, "kv_write": write}
+
+
+def host_array(t):
+    """Device tensor -> numpy in the oracle's storage (uint16 bit patterns for bf16)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_baseline(cfg, q, k_cache, v_cache, table, lens, nseq):
+    """The oracle, single-threaded BLAS, on the first ``nseq`` sequences."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    nseq = min(nseq, cfg.num_seqs)
+    seqs = list(range(nseq))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, k_cache, v_cache, table, lens, cfg.scale, cfg.dtype, seqs=seqs)
+        dt = time.perf_counter() - t0
+    sub = np.asarray(lens[:nseq], dtype=np.int64)
+    kv = int(sub.sum()) * cfg.kv_heads * cfg.head_dim * cfg.elem_bytes * 2
+    return {
+        "value": round(kv / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "seqs_per_s": round(nseq / dt, 3),
+        "wall_s": round(dt, 3),
+        "sample": f"first {nseq} of {cfg.num_seqs} sequences of the same batch (same pools), "
+                  f"one decode step, fp64 numpy, BLAS limited to 1 thread",
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_317_amd as pkv
+    from paged_kv_cache_317_amd.build import ensure_built
+    from workloads import generate_device, get_config, scaled
+
+    ensure_built()
+    cfg = get_config(args.workload)
+    if args.part_tokens is not None:
+        cfg = scaled(cfg, part_tokens=args.part_tokens)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"# workload {cfg.name}: generating on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    w = generate_device(cfg, device=dev)
+    lay = w.layout
+    max_len = lay.max_seq_len
+    out = torch.empty_like(w.q)
+    ws_bytes = pkv.decode_workspace_size(w.k_cache, cfg.num_seqs, cfg.q_heads, max_len,
+                                         cfg.part_tokens)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    part = pkv.decode_partition_tokens(w.k_cache, cfg.num_seqs, cfg.q_heads, max_len,
+                                       cfg.part_tokens)
+
+    def write():
+        pkv.paged_kv_write(w.new_k, w.new_v, w.slot_mapping, w.k_cache, w.v_cache)
+
+    def decode():
+        pkv.paged_attn_decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, cfg.scale,
+                              max_len, out=out, part_tokens=cfg.part_tokens, workspace=ws)
+
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        write()
+        ev[i][0].record()
+        decode()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = wall * 1e3 / K
+    print(f"# {K} steps: {step_ms:.4f} ms/step, decode {decode_ms:.4f} ms", file=sys.stderr,
+          flush=True)
+
+    nb = step_bytes(cfg, lay.seq_lens)
+    step_total = nb["decode"] + nb["kv_write"]
+    value = step_total / (step_ms * 1e-3) / 1e9
+    achieved = nb["decode"] / (decode_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_sample > 0:
+        print(f"# cpu baseline: oracle on {args.cpu_sample} sequences", file=sys.stderr,
+              flush=True)
+        q, kc, vc = (host_array(t) for t in (w.q, w.k_cache, w.v_cache))
+        cpu = cpu_baseline(cfg, q, kc, vc, lay.block_table, lay.seq_lens, args.cpu_sample)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded, drawn on the device)",
+        "config": {
+            "workload": cfg.name,
+            "num_seqs": cfg.num_seqs,
+            "q_heads": cfg.q_heads,
+            "kv_heads": cfg.kv_heads,
+            "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size,
+            "seq_lens": [int(lay.seq_lens.min()), int(lay.seq_lens.max())],
+            "pool_blocks": lay.num_blocks,
+            "part_tokens": part,
+            "step": "paged_kv_write (one token per sequence) + paged_attn_decode",
+        },
+        "seqs_per_s": round(cfg.num_seqs / (step_ms * 1e-3), 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_ms": round(decode_ms, 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attn_decode" + (" (partition + merge)" if part < max_len else ""),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": nb["decode"],
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,189 @@
+/*
+ * pkv.h - C ABI of libpkv: paged KV-cache decode attention for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The cache of one attention layer is split into fixed-size physical blocks,
+ * each holding the keys (one array) or values (a second array) of
+ * `block_size` consecutive tokens of one sequence; a per-sequence block table
+ * maps logical block j (token positions j*block_size .. j*block_size +
+ * block_size - 1) to a physical block anywhere in the pool ("PagedAttention
+ * Explained: Virtual Memory for the KV Cache", section "How PagedAttention
+ * works", steps 1-3).  Three operations act on such a cache:
+ *
+ *   pkv_paged_kv_write     store new tokens' K/V rows in their slots
+ *   pkv_paged_attn_decode  attention of one query token per sequence,
+ *                          gathering K/V through the block table (step 5)
+ *   pkv_paged_block_copy   copy whole blocks, the copy step of copy-on-write
+ *                          ("Sharing blocks between sequences")
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every buffer argument is a device pointer to memory the caller
+ *           allocated (hipMalloc or a framework allocator) and keeps alive
+ *           until the work on `stream` has finished.  The library never
+ *           allocates, frees or synchronises; it launches kernels on
+ *           `stream` (a hipStream_t passed as void*; NULL is the default
+ *           stream) and returns before they run.
+ * Layouts.  All arrays are dense and row-major.
+ *           cache:  [num_blocks, block_size, kv_heads, head_dim] of `dtype`;
+ *                   the row of slot `s` (token offset s % block_size of
+ *                   physical block s / block_size) starts at element
+ *                   s * kv_heads * head_dim.
+ *           q, out: [num_seqs, q_heads, head_dim] of the cache dtype.
+ *           bf16 is IEEE binary32's upper 16 bits (bfloat16).
+ *           Cache, q, k, v and out pointers must be 16-byte aligned.
+ * Errors.   Arguments are checked on the host before anything is launched;
+ *           on any failure nothing is launched and a non-zero pkv_status is
+ *           returned, with a message from pkv_last_error().  PKV_ERR_HIP
+ *           reports a launch error from the HIP runtime.  Faults while the
+ *           kernels run surface at the caller's next synchronisation.
+ * Device-side safety.  Values read from device memory (slots, table entries,
+ *           copy pairs) cannot be checked on the host.  Kernels never touch
+ *           memory outside the pool for an id outside it: such a slot or copy
+ *           pair is skipped, and decode stops reading a sequence's partition
+ *           at such a table entry (the output for that sequence is then
+ *           unspecified).  That is a guard, not a contract: callers must
+ *           pass valid ids.
+ * Threads.  The library keeps no state between calls apart from the
+ *           thread-local last-error message, so calls from several host
+ *           threads are safe; ordering between them is the streams'.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  PKV_ERR_SHAPE = 2,       /* a size is negative, zero or inconsistent       */
+  PKV_ERR_DTYPE = 3,       /* unknown dtype code                             */
+  PKV_ERR_UNSUPPORTED = 4, /* well-formed, but no kernel is built for it     */
+  PKV_ERR_WORKSPACE = 5,   /* split decode needs a (larger) workspace        */
+  PKV_ERR_HIP = 6,         /* the HIP runtime rejected a launch              */
+  PKV_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned               */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Shape of one layer's paged cache (K and V have the same shape). */
+typedef struct {
+  int32_t num_blocks; /* physical blocks in the pool, >= 1                  */
+  int32_t block_size; /* token slots per block                              */
+  int32_t kv_heads;   /* key/value heads per token                          */
+  int32_t head_dim;   /* elements per head                                  */
+  int32_t dtype;      /* pkv_dtype of the cache, q, k, v and out            */
+} pkv_cache_desc;
+
+/*
+ * Slot write.  For every token i < num_tokens with 0 <= slot_mapping[i] <
+ * num_blocks*block_size, copies k[i] and v[i] (each [kv_heads, head_dim])
+ * into the row of slot slot_mapping[i] of k_cache and v_cache, bit for bit.
+ * Negative slots are padding and write nothing.  Two tokens naming the same
+ * slot in one call leave that slot holding one of them (unspecified which).
+ * The cache grows by one such row per new token and layer ("PagedAttention
+ * Explained", "The problem: the KV cache is big and unpredictable"); the
+ * slot is physical_block * block_size + offset (same page, "How
+ * PagedAttention works", steps 2-4).
+ *   k, v          device, [num_tokens, kv_heads, head_dim], cache dtype
+ *   slot_mapping  device, int64 [num_tokens]
+ *   k_cache, v_cache  device, written in place
+ * Supported: f32 or bf16 with head_dim * element size a multiple of 16
+ * bytes.  num_tokens == 0 is a no-op (pointers may then be NULL).
+ */
+pkv_status pkv_paged_kv_write(const void* k, const void* v,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              void* k_cache, void* v_cache,
+                              const pkv_cache_desc* cache, void* stream);
+
+/*
+ * Decode attention over a paged cache.  For each sequence s with length
+ * L = seq_lens[s] and each query head h, with G = q_heads / kv_heads and
+ * kv head g = h / G:
+ *     out[s,h,:] = sum_{t<L} softmax_t(scale * q[s,h,:] . K_s[t,g,:]) V_s[t,g,:]
+ * where K_s[t] is the row at offset t % block_size of physical block
+ * block_table[s, t / block_size], and likewise V_s ("PagedAttention
+ * Explained", "How PagedAttention works", steps 2, 3 and 5; the pages print
+ * no formula, and this is standard scaled-dot-product attention of one
+ * query token).  L == 0 gives a zero row.  Arithmetic is fp32 (bf16 inputs
+ * are widened exactly; the output is rounded to nearest even for bf16).
+ *   q            device, [num_seqs, q_heads, head_dim]
+ *   k_cache, v_cache  device, read only
+ *   block_table  device, int32 [num_seqs, table_width]; entries at or past
+ *                ceil(L / block_size) are never read
+ *   seq_lens     device, int32 [num_seqs]
+ *   max_seq_len  host-side bound on every seq_lens[s] (sizes the grid without
+ *                reading device memory); a sequence is cut to
+ *                min(seq_lens[s], max_seq_len, table_width * block_size)
+ *   scale        softmax scale, typically 1/sqrt(head_dim)
+ *   out          device, [num_seqs, q_heads, head_dim], written
+ *   part_tokens  split-K partition length in tokens (rounded up to a
+ *                multiple of block_size), or 0 to let the library choose;
+ *                pkv_decode_partition_tokens() reports the choice
+ *   workspace    device scratch of at least pkv_decode_workspace_size()
+ *                bytes when the call splits (more than one partition);
+ *                may be NULL when that size is 0.  Contents need no
+ *                initialisation and are left undefined.
+ * Supported: f32 with head_dim 64, bf16 with head_dim 128; block_size 16 or
+ * 32; G in {1, 2, 4, 8}.
+ */
+pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,
+                                 const void* v_cache,
+                                 const pkv_cache_desc* cache,
+                                 const int32_t* block_table,
+                                 int32_t table_width, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t q_heads,
+                                 int32_t max_seq_len, float scale, void* out,
+                                 int32_t part_tokens, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Partition length (tokens) pkv_paged_attn_decode uses for these arguments;
+ * the call is split when it is below max_seq_len.  Returns 0 on invalid
+ * arguments (see pkv_last_error()).
+ */
+int32_t pkv_decode_partition_tokens(const pkv_cache_desc* cache,
+                                    int32_t num_seqs, int32_t q_heads,
+                                    int32_t max_seq_len, int32_t part_tokens);
+
+/*
+ * Workspace bytes pkv_paged_attn_decode needs for these arguments (0 when it
+ * does not split).  Returns 0 on invalid arguments as well; check
+ * pkv_last_error() when in doubt.
+ */
+size_t pkv_decode_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
+                                 int32_t q_heads, int32_t max_seq_len,
+                                 int32_t part_tokens);
+
+/*
+ * Block copy.  For each pair i < num_pairs, (src, dst) = (pairs[2i],
+ * pairs[2i+1]), the whole block dst of k_cache and of v_cache becomes a bit
+ * copy of block src: the copy taken before a sequence writes into a block
+ * that other sequences still share, after which the writer's table points
+ * at dst ("PagedAttention Explained", "Sharing blocks between sequences").
+ * Within one call the dst ids must be distinct and no dst may equal a src;
+ * pairs with an id outside [0, num_blocks) are skipped.
+ *   pairs        device, int64 [num_pairs, 2]
+ *   k_cache, v_cache  device, written in place
+ * num_pairs == 0 is a no-op.
+ */
+pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pairs,
+                                void* k_cache, void* v_cache,
+                                const pkv_cache_desc* cache, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

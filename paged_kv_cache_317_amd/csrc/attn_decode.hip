@@ -1,0 +1,429 @@
+// Block-aware decode attention for gfx950.
+//
+// One query token per sequence attends over that sequence's cached keys and
+// values, which live in fixed-size physical blocks reached through the
+// sequence's block table ("PagedAttention Explained: Virtual Memory for the KV
+// Cache", section "How PagedAttention works", steps 2, 3 and 5).  The result is
+// standard scaled-dot-product softmax attention per query head; query head h
+// reads kv head h / G (grouped-query attention, "Trade-offs and related
+// techniques").
+//
+// Work decomposition
+//   unit      = (sequence, partition, group of kv heads) -> one workgroup
+//   wave      = one kv head of the unit and its G query heads
+//   tile      = 16 consecutive token positions (a block of 16 is one tile,
+//               a block of 32 two)
+// A workgroup stages its partition's slice of the block table in LDS once;
+// each wave then walks the tiles, loading the next tile's K and V rows while
+// it computes on the current one.
+//
+// Per tile (one wave):
+//   logits   q . K^T with one MFMA chain: the 16 tokens are the M rows (A
+//            operand, K rows as stored), the group's query heads the N
+//            columns (B operand, columns >= G hold zero).  bf16 uses
+//            v_mfma_f32_16x16x32_bf16 (exact products, fp32 sums); f32 uses
+//            v_mfma_f32_16x16x4_f32.
+//   softmax  running max and sum per head (online softmax in base 2, the
+//            scale folded with log2 e); the output lanes of column h hold
+//            head h, four tokens per lane, so the tile max is an in-lane max
+//            plus two cross-row exchanges.
+//   P.V      fp32 FMAs: lane (r, c) owns 16-byte chunk c of the value rows
+//            of tokens 4r..4r+3 and accumulates all G heads; the weight of
+//            (token, head) comes from the logits lane of the same 16-lane row
+//            by DPP row broadcast.
+// Loads: K tile = four 16-byte loads per lane (16 rows x 64 contiguous bytes
+// per instruction), V tile = four 16-byte loads per lane (4 rows x 256
+// contiguous bytes per instruction).  Every cached byte a sequence needs is
+// read exactly once per call.
+//
+// Split-K (long contexts): with more than one partition per sequence each
+// wave writes its unnormalised state (max, sum, o[D]) per head to the
+// workspace and a second kernel merges the partitions with the log-sum-exp
+// rule in a fixed order (deterministic, no atomics).
+#include <utility>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;
+
+template <typename T>
+struct Storage;
+template <>
+struct Storage<float> {
+  static constexpr int kPerVec = 4;    // elements per 16-byte chunk
+};
+template <>
+struct Storage<uint16_t> {             // bf16 held as raw bits
+  static constexpr int kPerVec = 8;
+};
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Logits of one 16-token tile: acc[i] in lane (r, c) is q_head(c) . K_token(4r + i).
+__device__ __forceinline__ f32x4_t tile_logits(const u32x4_t (&k)[4], const u32x4_t (&q)[4],
+                                               uint16_t) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k[c]),
+                                                  __builtin_bit_cast(bf16x8_t, q[c]), acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4_t tile_logits(const u32x4_t (&k)[4], const u32x4_t (&q)[4],
+                                               float) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[c][e]), __uint_as_float(q[c][e]),
+                                                 acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ void unpack(const u32x4_t& w, float (&f)[8], uint16_t) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = bf16_lo(w[j]);
+    f[2 * j + 1] = bf16_hi(w[j]);
+  }
+}
+__device__ __forceinline__ void unpack(const u32x4_t& w, float (&f)[4], float) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(w[j]);
+}
+
+template <int E>
+__device__ __forceinline__ void store_row(void* dst, const float (&f)[E], float mul, uint16_t) {
+  u32x4_t w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = f32_to_bf16_bits(f[2 * j] * mul) | (f32_to_bf16_bits(f[2 * j + 1] * mul) << 16);
+  *reinterpret_cast<u32x4_t*>(dst) = w;
+}
+template <int E>
+__device__ __forceinline__ void store_row(void* dst, const float (&f)[E], float mul, float) {
+  u32x4_t w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(f[j] * mul);
+  *reinterpret_cast<u32x4_t*>(dst) = w;
+}
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_size) {
+  int L = a.seq_lens[s];
+  L = min(L, a.max_seq_len);
+  L = min(L, a.table_width * block_size);
+  return max(L, 0);
+}
+
+template <typename T, int D, int BS, int G>
+__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+  constexpr int E = Storage<T>::kPerVec;
+  static_assert(D / E == 16, "a token row must be sixteen 16-byte chunks");
+  static_assert(BS % kTile == 0, "block_size must be a multiple of 16");
+  static_assert(G >= 1 && G <= 16, "query heads per kv head must fit the 16 MFMA columns");
+  constexpr int kTilesPerBlock = BS / kTile;
+
+  __shared__ int32_t s_table[kMaxPartBlocks];
+
+  const int lane = threadIdx.x & 63;
+  const int rg = lane >> 4;            // row group: logits rows 4rg..4rg+3, V tokens 4rg..4rg+3
+  const int lc = lane & 15;            // K row / query head column / V chunk
+  const int groups = a.kv_heads / a.heads_per_wg;
+  int unit = blockIdx.x;
+  const int grp = unit % groups;
+  unit /= groups;
+  const int part = unit % a.num_parts;
+  const int s = unit / a.num_parts;
+  const int g = grp * a.heads_per_wg + (threadIdx.x >> 6);
+
+  const int L = clamp_len(a, s, BS);
+  const int t0 = part * a.part_tokens;
+  if (a.num_parts > 1 && t0 >= L) return;          // uniform over the workgroup
+  int t1 = min(L, t0 + a.part_tokens);
+  const int nblk = max(t1 - t0, 0) / BS + ((max(t1 - t0, 0) % BS) != 0);
+  const int j0 = t0 / BS;
+
+  // The partition's slice of the block table, once per workgroup.  A table
+  // entry outside the pool ends the sequence at that block: the partition is
+  // cut back to the first such entry.
+  __shared__ int s_first_bad;
+  if (threadIdx.x == 0) s_first_bad = nblk;
+  __syncthreads();
+  for (int j = threadIdx.x; j < nblk; j += blockDim.x) {
+    const int b = a.block_table[(int64_t)s * a.table_width + j0 + j];
+    s_table[j] = b;
+    if (b < 0 || b >= a.num_blocks) atomicMin(&s_first_bad, j);
+  }
+  __syncthreads();
+  t1 = min(t1, t0 + s_first_bad * BS);
+  const int ntok = max(t1 - t0, 0);
+
+  // Query heads hq0 .. hq0+G-1 as the MFMA B operand (same chunk order as K).
+  const int hq0 = g * G;
+  u32x4_t qv[4];
+  {
+    // Columns >= G read head G-1 and are then zeroed (no branch around loads).
+    const int hc = min(lc, G - 1);
+    const T* qrow = reinterpret_cast<const T*>(a.q) + ((int64_t)s * a.q_heads + hq0 + hc) * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + (rg + 4 * c) * E);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[c][j] = lc < G ? w[j] : 0u;
+    }
+  }
+
+  // Byte offsets.  A tile's rows start at a wave-uniform address (SGPR pair);
+  // each lane adds fixed 32-bit offsets, so every load is SGPR base + VGPR
+  // offset (+ immediate).
+  const uint32_t row_u32 = a.row_bytes;                                  // one slot
+  const uint32_t head_bytes = (uint32_t)(g * D * sizeof(T));
+  const uint32_t k_lane = lc * row_u32 + head_bytes + rg * 16;          // + c * 64
+  const uint32_t v_lane0 = 4 * rg * row_u32 + head_bytes + lc * 16;     // token 4rg
+  const char* kcache = reinterpret_cast<const char*>(a.k_cache);
+  const char* vcache = reinterpret_cast<const char*>(a.v_cache);
+
+  float m_run = -INFINITY;   // per column (head), in log2 units
+  float l_run = 0.f;         // per lane: this row group's share of the sum
+  float o[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+
+  auto load_tile = [&](int tile, u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
+    const uint32_t phys = (uint32_t)uniform_int(s_table[tile / kTilesPerBlock]);
+    const uint64_t base = (uint64_t)phys * a.block_bytes +
+                          (uint32_t)((tile % kTilesPerBlock) * a.tile_bytes);
+    const char* kp = kcache + base;
+    const char* vp = vcache + base;
+    // The offsets are re-materialised here so that each load is selected as
+    // SGPR base + 32-bit VGPR offset rather than a 64-bit VGPR address.
+    uint32_t kl = k_lane, v0 = v_lane0, v1 = v_lane0 + row_u32, v2 = v_lane0 + 2 * row_u32,
+             v3 = v_lane0 + 3 * row_u32;
+    asm volatile("" : "+v"(kl), "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const u32x4_t*>(kp + kl + c * 64);
+    vr[0] = *reinterpret_cast<const u32x4_t*>(vp + v0);
+    vr[1] = *reinterpret_cast<const u32x4_t*>(vp + v1);
+    vr[2] = *reinterpret_cast<const u32x4_t*>(vp + v2);
+    vr[3] = *reinterpret_cast<const u32x4_t*>(vp + v3);
+  };
+
+  // One tile: logits, online-softmax update, P.V.  kMasked handles the one
+  // ragged tile at the end of a partition: tokens at or past t1 get weight 0
+  // and their value rows (unused slots, any bits) are replaced by zeros.
+  auto process = [&](auto masked, int tile, const u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const int tb = t0 + tile * kTile;
+    const f32x4_t acc = tile_logits(kr, qv, T{});
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = acc[i] * a.scale_log2;
+      if (kMasked && tb + 4 * rg + i >= t1) x[i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = max_xor32(max_xor16(mx));
+    // Every tile holds at least one unmasked token, so m_new is finite.
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m_run = m_new;
+    if (__any(lc < G && alpha != 1.f)) {
+      static_for<G>([&](auto H) {
+        const float al = read_lane(alpha, H);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[H][e] *= al;
+      });
+    }
+    if constexpr (kMasked) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool keep = tb + 4 * rg + i < t1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vr[i][j] = keep ? vr[i][j] : 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float vf[E];
+      unpack(vr[i], vf, T{});
+      static_for<G>([&](auto H) {
+        const float ph = row_bcast<H>(p[i]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[H][e] = fmaf(ph, vf[e], o[H][e]);
+      });
+    }
+  };
+
+  // Two register sets, refilled as soon as they are consumed: while one tile
+  // is computed the next is in flight.  Tiles 0 .. nfull-1 are full; a
+  // ragged tile, if any, is the last one and goes through the masked path.
+  // Loads past the last tile re-read it (an L2 hit) so that every iteration
+  // issues the same loads.
+  const int ntiles = (ntok + kTile - 1) / kTile;
+  const int nfull = ntok / kTile;
+  if (ntiles > 0) {
+    const std::false_type full{};
+    const std::true_type ragged{};
+    u32x4_t ka[4], va[4], kb[4], vb[4];
+    load_tile(0, ka, va);
+    load_tile(min(1, ntiles - 1), kb, vb);
+    for (int t = 0;; t += 2) {
+      if (t == nfull) {
+        process(ragged, t, ka, va);
+        break;
+      }
+      process(full, t, ka, va);
+      if (t + 1 >= ntiles) break;
+      load_tile(min(t + 2, ntiles - 1), ka, va);
+      if (t + 1 == nfull) {
+        process(ragged, t + 1, kb, vb);
+        break;
+      }
+      process(full, t + 1, kb, vb);
+      if (t + 2 >= ntiles) break;
+      load_tile(min(t + 3, ntiles - 1), kb, vb);
+    }
+  }
+
+  // Sum the four row groups' shares.
+  const float l_tot = sum_xor32(sum_xor16(l_run));
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[h][e] = sum_xor32(sum_xor16(o[h][e]));
+
+  static_for<G>([&](auto H) {
+    constexpr int h = H;
+    const float l_h = read_lane(l_tot, h);
+    const float m_h = read_lane(m_run, h);
+    if (rg == (h & 3)) {
+      const int64_t orow = (int64_t)s * a.q_heads + hq0 + h;
+      if (a.num_parts == 1) {
+        const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
+        store_row<E>(reinterpret_cast<T*>(a.out) + orow * D + lc * E, o[h], inv, T{});
+      } else {
+        const int64_t slot = orow * a.num_parts + part;
+        float* po = a.part_o + slot * D + lc * E;
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *reinterpret_cast<f32x4_t*>(po + e) = f32x4_t{o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]};
+        if (lc == 0) {
+          a.part_ml[2 * slot] = m_h;
+          a.part_ml[2 * slot + 1] = l_h;
+        }
+      }
+    }
+  });
+}
+
+// Merge of the partition states of one (sequence, query head) row:
+// M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p.
+template <typename T, int D, int BS>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x;
+  const int orow = blockIdx.x;
+  const int s = orow / a.q_heads;
+  const int L = clamp_len(a, s, BS);
+  const int P = (L + a.part_tokens - 1) / a.part_tokens;
+  const float* ml = a.part_ml + (int64_t)orow * a.num_parts * 2;
+  const float* po = a.part_o + (int64_t)orow * a.num_parts * D + lane * PER;
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, ml[2 * p]);
+  float lsum = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int p = 0; p < P; ++p) {
+    // A partition with no tokens (m = -inf) carries no weight.
+    const float w = ml[2 * p] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[2 * p] - M);
+    lsum = fmaf(w, ml[2 * p + 1], lsum);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[(int64_t)p * D + e], acc[e]);
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  T* out = reinterpret_cast<T*>(a.out) + (int64_t)orow * D + lane * PER;
+  if constexpr (sizeof(T) == 2) {
+    static_assert(PER == 2, "bf16 reduce writes two elements per lane");
+    *reinterpret_cast<uint32_t*>(out) =
+        f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = acc[e] * inv;
+  }
+}
+
+template <typename T, int D, int BS, int G>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int groups = a.kv_heads / a.heads_per_wg;
+  const int64_t units = (int64_t)a.num_seqs * a.num_parts * groups;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, G>), dim3((unsigned)units),
+                     dim3(64 * a.heads_per_wg), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.num_parts == 1) return err;
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D, BS>), dim3((unsigned)(a.num_seqs * a.q_heads)),
+                     dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+typedef hipError_t (*Launcher)(const DecodeArgs&, hipStream_t);
+
+template <typename T, int D, int BS>
+Launcher pick_group(int group) {
+  switch (group) {
+    case 1: return launch_typed<T, D, BS, 1>;
+    case 2: return launch_typed<T, D, BS, 2>;
+    case 4: return launch_typed<T, D, BS, 4>;
+    case 8: return launch_typed<T, D, BS, 8>;
+    default: return nullptr;
+  }
+}
+
+Launcher pick(int dtype, int head_dim, int block_size, int group) {
+  if (dtype == 1 && head_dim == 128) {
+    if (block_size == 16) return pick_group<uint16_t, 128, 16>(group);
+    if (block_size == 32) return pick_group<uint16_t, 128, 32>(group);
+  }
+  if (dtype == 0 && head_dim == 64) {
+    if (block_size == 16) return pick_group<float, 64, 16>(group);
+    if (block_size == 32) return pick_group<float, 64, 32>(group);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+bool decode_supported(int dtype, int head_dim, int block_size, int group) {
+  return pick(dtype, head_dim, block_size, group) != nullptr;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
+                         hipStream_t stream) {
+  Launcher f = pick(dtype, head_dim, block_size, group);
+  if (!f) return hipErrorInvalidValue;
+  return f(a, stream);
+}
+
+}  // namespace pkv

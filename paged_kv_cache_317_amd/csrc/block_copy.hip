@@ -1,0 +1,58 @@
+// Block copy: for every (src, dst) pair the whole physical block dst of the K
+// pool and of the V pool becomes a bit copy of block src.  This is the copy
+// step of copy-on-write: a sequence about to write into a block that other
+// sequences still reference gets its own copy first ("PagedAttention
+// Explained", "Sharing blocks between sequences").
+//
+// Work split: each workgroup copies one 16 KiB chunk of one block of one pool;
+// every thread issues all its loads before its stores so that four 16-byte
+// loads per thread are in flight.  Pure data movement, HBM bound.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecsPerThread = 4;
+constexpr int kChunkVecs = kThreads * kVecsPerThread;   // 16 KiB
+
+__global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a, int chunks) {
+  const int per_pair = 2 * chunks;
+  const int pair = blockIdx.x / per_pair;
+  const int rem = blockIdx.x - pair * per_pair;
+  const int pool = rem / chunks;                   // 0: K, 1: V
+  const int chunk = rem - pool * chunks;
+  const int64_t src = a.pairs[2 * pair];
+  const int64_t dst = a.pairs[2 * pair + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  const int64_t block_vecs = a.block_bytes >> 4;
+  uint4* base = reinterpret_cast<uint4*>(pool ? a.v_cache : a.k_cache);
+  const uint4* from = base + src * block_vecs;
+  uint4* to = base + dst * block_vecs;
+  const int64_t first = (int64_t)chunk * kChunkVecs + threadIdx.x;
+  uint4 buf[kVecsPerThread];
+#pragma unroll
+  for (int i = 0; i < kVecsPerThread; ++i) {
+    const int64_t e = first + i * kThreads;
+    if (e < block_vecs) buf[i] = from[e];
+  }
+#pragma unroll
+  for (int i = 0; i < kVecsPerThread; ++i) {
+    const int64_t e = first + i * kThreads;
+    if (e < block_vecs) to[e] = buf[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream) {
+  if (a.num_pairs == 0) return hipSuccess;
+  const int64_t block_vecs = a.block_bytes >> 4;
+  const int chunks = (int)((block_vecs + kChunkVecs - 1) / kChunkVecs);
+  const int64_t grid = (int64_t)a.num_pairs * 2 * chunks;
+  hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

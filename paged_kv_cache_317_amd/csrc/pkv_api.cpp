@@ -1,0 +1,255 @@
+// C ABI of libpkv: argument checks, the split decision, and dispatch to the
+// kernel launchers.  Every check runs on the host before any HIP call, so an
+// invalid call launches nothing and touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "kernels.hpp"
+
+#define PKV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+pkv_status from_hip(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+pkv_status check_cache(const pkv_cache_desc* c) {
+  if (!c) return fail(PKV_ERR_NULL, "cache descriptor is NULL");
+  if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+    return fail(PKV_ERR_DTYPE, "unknown dtype code %d", (int)c->dtype);
+  if (c->num_blocks < 1 || c->block_size < 1 || c->kv_heads < 1 || c->head_dim < 1)
+    return fail(PKV_ERR_SHAPE, "cache sizes must be positive (num_blocks %d, block_size %d, "
+                "kv_heads %d, head_dim %d)", (int)c->num_blocks, (int)c->block_size,
+                (int)c->kv_heads, (int)c->head_dim);
+  const int64_t row = (int64_t)c->head_dim * elem_bytes(c->dtype);
+  if (row % 16) return fail(PKV_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
+  return PKV_OK;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Split policy.  A partition is the unit of work of one wave per kv head; the
+// grid has num_seqs * kv_heads * partitions waves.  Without an explicit
+// request the call stays unsplit while that already gives enough waves to
+// fill the GPU (about 8 per CU on 256 CUs), and otherwise halves the
+// partition length (down to 512 tokens) until it does.  A partition never
+// exceeds the LDS table slice.
+constexpr int64_t kWaveTarget = 2048;
+constexpr int64_t kMinAutoPart = 512;
+
+int64_t part_tokens_for(const pkv_cache_desc& c, int64_t num_seqs, int64_t max_seq_len,
+                        int64_t requested) {
+  const int64_t BS = c.block_size;
+  const int64_t cap = (int64_t)pkv::kMaxPartBlocks * BS;
+  if (requested > 0) return requested >= cap ? cap : round_up(requested, BS);
+  int64_t pt = round_up(max_seq_len > 0 ? max_seq_len : 1, BS);
+  if (pt > cap) pt = cap;
+  const int64_t floor_pt = round_up(kMinAutoPart, BS);
+  auto waves = [&](int64_t p) { return num_seqs * c.kv_heads * ((max_seq_len + p - 1) / p); };
+  while (pt > floor_pt && waves(pt) < kWaveTarget) pt = round_up(pt / 2, BS);
+  return pt;
+}
+
+struct DecodePlan {
+  int64_t part_tokens = 0;
+  int64_t num_parts = 1;
+  size_t workspace = 0;
+};
+
+pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_heads,
+                       int32_t max_seq_len, int32_t part_tokens, DecodePlan* plan) {
+  pkv_status st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_seq_len < 0 || part_tokens < 0)
+    return fail(PKV_ERR_SHAPE, "num_seqs, max_seq_len and part_tokens must be >= 0");
+  if (q_heads < 1 || q_heads % c->kv_heads)
+    return fail(PKV_ERR_SHAPE, "q_heads (%d) must be a positive multiple of kv_heads (%d)",
+                (int)q_heads, (int)c->kv_heads);
+  const int group = q_heads / c->kv_heads;
+  if (!pkv::decode_supported(c->dtype, c->head_dim, c->block_size, group))
+    return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for dtype %d, head_dim %d, block_size %d, "
+                "group %d (built: f32 head_dim 64, bf16 head_dim 128; block 16 or 32; group 1, "
+                "2, 4 or 8)", (int)c->dtype, (int)c->head_dim, (int)c->block_size, group);
+  plan->part_tokens = part_tokens_for(*c, num_seqs, max_seq_len, part_tokens);
+  plan->num_parts = max_seq_len > 0 ? (max_seq_len + plan->part_tokens - 1) / plan->part_tokens : 1;
+  plan->workspace = 0;
+  if (plan->num_parts > 1) {
+    const int64_t rows = (int64_t)num_seqs * q_heads * plan->num_parts;
+    plan->workspace = (size_t)((round_up(2 * rows, 4) + rows * c->head_dim) * sizeof(float));
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+PKV_EXPORT const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+PKV_EXPORT const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+
+PKV_EXPORT pkv_status pkv_paged_kv_write(const void* k, const void* v, const int64_t* slot_mapping,
+                                         int64_t num_tokens, void* k_cache, void* v_cache,
+                                         const pkv_cache_desc* cache, void* stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_ERR_NULL, "k, v, slot_mapping, k_cache and v_cache must be non-NULL");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_ALIGN, "k, v, k_cache and v_cache must be 16-byte aligned");
+  pkv::KvWriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_slots = (int64_t)cache->num_blocks * cache->block_size;
+  a.row_bytes = (int64_t)cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype);
+  return from_hip(pkv::launch_kv_write(a, (hipStream_t)stream), "paged_kv_write launch");
+}
+
+PKV_EXPORT int32_t pkv_decode_partition_tokens(const pkv_cache_desc* cache, int32_t num_seqs,
+                                               int32_t q_heads, int32_t max_seq_len,
+                                               int32_t part_tokens) {
+  DecodePlan plan;
+  if (plan_decode(cache, num_seqs, q_heads, max_seq_len, part_tokens, &plan) != PKV_OK) return 0;
+  ok();
+  return (int32_t)plan.part_tokens;
+}
+
+PKV_EXPORT size_t pkv_decode_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
+                                            int32_t q_heads, int32_t max_seq_len,
+                                            int32_t part_tokens) {
+  DecodePlan plan;
+  if (plan_decode(cache, num_seqs, q_heads, max_seq_len, part_tokens, &plan) != PKV_OK) return 0;
+  ok();
+  return plan.workspace;
+}
+
+PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                            const pkv_cache_desc* cache, const int32_t* block_table,
+                                            int32_t table_width, const int32_t* seq_lens,
+                                            int32_t num_seqs, int32_t q_heads, int32_t max_seq_len,
+                                            float scale, void* out, int32_t part_tokens,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  pkv_status st = plan_decode(cache, num_seqs, q_heads, max_seq_len, part_tokens, &plan);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (table_width < 1) return fail(PKV_ERR_SHAPE, "table_width must be >= 1");
+  if ((int64_t)table_width * cache->block_size > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "table_width * block_size exceeds the int32 token range");
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+    return fail(PKV_ERR_NULL, "q, k_cache, v_cache, block_table, seq_lens and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (plan.workspace > 0) {
+    if (!workspace) return fail(PKV_ERR_WORKSPACE, "this call splits into %lld partitions and needs "
+                                "a %zu-byte workspace", (long long)plan.num_parts, plan.workspace);
+    if (workspace_bytes < plan.workspace)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
+                  workspace_bytes, plan.workspace);
+    if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  const int group = q_heads / cache->kv_heads;
+  int heads_per_wg = 1;
+  for (int w : {4, 2}) {
+    if (cache->kv_heads % w == 0) {
+      heads_per_wg = w;
+      break;
+    }
+  }
+  const int64_t block_bytes =
+      (int64_t)cache->block_size * cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype);
+  if (block_bytes > UINT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "a block of %lld bytes exceeds 4 GiB", (long long)block_bytes);
+  const int64_t units = (int64_t)num_seqs * plan.num_parts * (cache->kv_heads / heads_per_wg);
+  if (units > INT32_MAX || (int64_t)num_seqs * q_heads > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)units);
+
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.out = out;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.part_ml = nullptr;
+  a.part_o = nullptr;
+  if (plan.workspace > 0) {
+    const int64_t rows = (int64_t)num_seqs * q_heads * plan.num_parts;
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = a.part_ml + round_up(2 * rows, 4);
+  }
+  a.num_blocks = cache->num_blocks;
+  a.table_width = table_width;
+  a.num_seqs = num_seqs;
+  a.q_heads = q_heads;
+  a.kv_heads = cache->kv_heads;
+  a.max_seq_len = max_seq_len;
+  a.part_tokens = (int32_t)plan.part_tokens;
+  a.num_parts = (int32_t)plan.num_parts;
+  a.heads_per_wg = heads_per_wg;
+  a.row_bytes = (uint32_t)((int64_t)cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype));
+  a.tile_bytes = 16u * a.row_bytes;
+  a.block_bytes = (uint32_t)(cache->block_size * (int64_t)a.row_bytes);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(pkv::launch_decode(a, cache->dtype, cache->head_dim, cache->block_size, group,
+                                     (hipStream_t)stream),
+                  "paged_attn_decode launch");
+}
+
+PKV_EXPORT pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pairs, void* k_cache,
+                                           void* v_cache, const pkv_cache_desc* cache,
+                                           void* stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return fail(PKV_ERR_SHAPE, "num_pairs must be >= 0");
+  if (num_pairs == 0) return ok();
+  if (!pairs || !k_cache || !v_cache)
+    return fail(PKV_ERR_NULL, "pairs, k_cache and v_cache must be non-NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_ALIGN, "k_cache and v_cache must be 16-byte aligned");
+  pkv::BlockCopyArgs a;
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = cache->num_blocks;
+  a.block_bytes = (int64_t)cache->block_size * cache->kv_heads * cache->head_dim *
+                  elem_bytes(cache->dtype);
+  const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
+  if ((int64_t)num_pairs * 2 * chunks > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "too many pairs for one launch");
+  return from_hip(pkv::launch_block_copy(a, (hipStream_t)stream), "paged_block_copy launch");
+}

@@ -30,3 +30,10 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Build libpkv.so once if it is missing (never rebuilds an existing one)."""
+    from paged_kv_cache_317_amd.build import ensure_built
+    ensure_built()
