@@ -21,7 +21,6 @@ same batch.
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -44,7 +43,33 @@ def parse_args(argv=None):
                    help="split-K partition length (default: the workload's, else the library's)")
     p.add_argument("--cpu-sample", type=int, default=128,
                    help="sequences the oracle computes for the CPU baseline (0 skips it)")
+    p.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
+                   help="instead of the decode step, time a plain device-to-device copy of "
+                        "GIB GiB (the reference kernel for HBM byte counters)")
     return p.parse_args(argv)
+
+
+def copy_probe(gib, steps, warmup):
+    """Plain copy of a known size: its time gives a practical HBM ceiling and
+    its counter readings the scale of FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"copy_bytes": n, "ms_per_copy": round(ms, 5),
+                      "read_plus_write_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    return 0
 
 
 def step_bytes(cfg, lens):
@@ -104,6 +129,9 @@ def main(argv=None):
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         return 2
+
+    if args.copy_probe > 0:
+        return copy_probe(args.copy_probe, args.steps, args.warmup)
 
     import numpy as np
     import torch

@@ -17,20 +17,24 @@
 // each wave then walks the tiles, loading the next tile's K and V rows while
 // it computes on the current one.
 //
-// Per tile (one wave):
-//   logits   q . K^T with one MFMA chain: the 16 tokens are the M rows (A
-//            operand, K rows as stored), the group's query heads the N
-//            columns (B operand, columns >= G hold zero).  bf16 uses
-//            v_mfma_f32_16x16x32_bf16 (exact products, fp32 sums); f32 uses
-//            v_mfma_f32_16x16x4_f32.
+// Per tile (one wave), bf16 caches:
+//   logits   S = K q^T with v_mfma_f32_16x16x32_bf16: the 16 tokens are the M
+//            rows (A operand, K rows as stored), the group's query heads the
+//            N columns (B operand; columns >= G hold zero).  Products of bf16
+//            values are exact in fp32; sums are fp32.
 //   softmax  running max and sum per head (online softmax in base 2, the
-//            scale folded with log2 e); the output lanes of column h hold
-//            head h, four tokens per lane, so the tile max is an in-lane max
-//            plus two cross-row exchanges.
-//   P.V      fp32 FMAs: lane (r, c) owns 16-byte chunk c of the value rows
-//            of tokens 4r..4r+3 and accumulates all G heads; the weight of
-//            (token, head) comes from the logits lane of the same 16-lane row
-//            by DPP row broadcast.
+//            scale folded with log2 e).  Lane (r, c) holds tokens 4r..4r+3 of
+//            head c, so the tile max is an in-lane max plus two row swaps.
+//   P.V      O^T += V^T P^T with v_mfma_f32_16x16x16bf16_1k over eight 16-dim
+//            slices.  The logits tile's lane layout is exactly the B operand
+//            layout, so P never moves between lanes; it is split into two
+//            bf16 terms (hi + lo) whose sum keeps 16 significant bits, and
+//            both are multiplied in.  V^T comes from the V tile staged in LDS
+//            (padded rows) through ds_read_b64_tr_b16 transpose reads.
+//            The accumulators are 8 x 4 fp32 per lane for any G <= 16.
+// f32 caches use v_mfma_f32_16x16x4_f32 for the logits and fp32 FMAs for P.V
+// (each lane owns one 16-byte chunk of the value rows of four tokens).
+//
 // Loads: K tile = four 16-byte loads per lane (16 rows x 64 contiguous bytes
 // per instruction), V tile = four 16-byte loads per lane (4 rows x 256
 // contiguous bytes per instruction).  Every cached byte a sequence needs is
@@ -49,8 +53,12 @@ namespace pkv {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kTile = 16;
+constexpr int kMaxWavesPerWg = 4;
 
 template <typename T>
 struct Storage;
@@ -95,34 +103,6 @@ __device__ __forceinline__ f32x4_t tile_logits(const u32x4_t (&k)[4], const u32x
   return acc;
 }
 
-__device__ __forceinline__ void unpack(const u32x4_t& w, float (&f)[8], uint16_t) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[2 * j] = bf16_lo(w[j]);
-    f[2 * j + 1] = bf16_hi(w[j]);
-  }
-}
-__device__ __forceinline__ void unpack(const u32x4_t& w, float (&f)[4], float) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(w[j]);
-}
-
-template <int E>
-__device__ __forceinline__ void store_row(void* dst, const float (&f)[E], float mul, uint16_t) {
-  u32x4_t w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    w[j] = f32_to_bf16_bits(f[2 * j] * mul) | (f32_to_bf16_bits(f[2 * j + 1] * mul) << 16);
-  *reinterpret_cast<u32x4_t*>(dst) = w;
-}
-template <int E>
-__device__ __forceinline__ void store_row(void* dst, const float (&f)[E], float mul, float) {
-  u32x4_t w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(f[j] * mul);
-  *reinterpret_cast<u32x4_t*>(dst) = w;
-}
-
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_size) {
   int L = a.seq_lens[s];
   L = min(L, a.max_seq_len);
@@ -130,18 +110,33 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_s
   return max(L, 0);
 }
 
+// Occupancy request: waves per SIMD the register allocation must allow.
+#ifndef PKV_DECODE_WAVES_PER_EU
+#define PKV_DECODE_WAVES_PER_EU 2
+#endif
+
 template <typename T, int D, int BS, int G>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
+void decode_partition_kernel(DecodeArgs a) {
+  constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int E = Storage<T>::kPerVec;
   static_assert(D / E == 16, "a token row must be sixteen 16-byte chunks");
   static_assert(BS % kTile == 0, "block_size must be a multiple of 16");
   static_assert(G >= 1 && G <= 16, "query heads per kv head must fit the 16 MFMA columns");
   constexpr int kTilesPerBlock = BS / kTile;
+  // bf16: one V tile per wave in LDS, rows padded by 32 bytes so that the
+  // transpose reads of a 16-lane group hit distinct banks.
+  constexpr int kVRow = D * 2 + 32;
+  constexpr int kVTileBytes = kBf16 ? kTile * kVRow : 16;
+  constexpr int kDimTiles = D / 16;
 
   __shared__ int32_t s_table[kMaxPartBlocks];
+  __shared__ int s_first_bad;
+  __shared__ __attribute__((aligned(16))) char s_vtile[kMaxWavesPerWg][kVTileBytes];
 
   const int lane = threadIdx.x & 63;
-  const int rg = lane >> 4;            // row group: logits rows 4rg..4rg+3, V tokens 4rg..4rg+3
+  const int wave = threadIdx.x >> 6;
+  const int rg = lane >> 4;            // row group: logits rows 4rg..4rg+3
   const int lc = lane & 15;            // K row / query head column / V chunk
   const int groups = a.kv_heads / a.heads_per_wg;
   int unit = blockIdx.x;
@@ -149,7 +144,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   unit /= groups;
   const int part = unit % a.num_parts;
   const int s = unit / a.num_parts;
-  const int g = grp * a.heads_per_wg + (threadIdx.x >> 6);
+  const int g = grp * a.heads_per_wg + wave;
 
   const int L = clamp_len(a, s, BS);
   const int t0 = part * a.part_tokens;
@@ -161,7 +156,6 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   // The partition's slice of the block table, once per workgroup.  A table
   // entry outside the pool ends the sequence at that block: the partition is
   // cut back to the first such entry.
-  __shared__ int s_first_bad;
   if (threadIdx.x == 0) s_first_bad = nblk;
   __syncthreads();
   for (int j = threadIdx.x; j < nblk; j += blockDim.x) {
@@ -198,13 +192,27 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   const char* kcache = reinterpret_cast<const char*>(a.k_cache);
   const char* vcache = reinterpret_cast<const char*>(a.v_cache);
 
+  // bf16 V tile in LDS: lane (r, c) writes chunk c of tokens 4r..4r+3; the
+  // transpose read of lane 16j + 4r' + q covers token 4j + r', dims 4q..4q+3
+  // of each 16-dim slice (offset 32 bytes per slice).
+  char* vt = s_vtile[wave];
+  const int tr_lane = (4 * rg + (lc >> 2)) * kVRow + 8 * (lc & 3);
+
   float m_run = -INFINITY;   // per column (head), in log2 units
   float l_run = 0.f;         // per lane: this row group's share of the sum
-  float o[G][E];
+  // bf16: O^T slices (lane (r, c): dims 16dt + 4r .. +3 of head c);
+  // f32: O rows (lane (r, c): chunk c of every head, tokens of row group r).
+  f32x4_t ot[kBf16 ? kDimTiles : 1];
+  float o[kBf16 ? 1 : G][E];
+  if constexpr (kBf16) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int dt = 0; dt < kDimTiles; ++dt) ot[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+  }
 
   auto load_tile = [&](int tile, u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
     const uint32_t phys = (uint32_t)uniform_int(s_table[tile / kTilesPerBlock]);
@@ -248,13 +256,6 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
     l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;
-    if (__any(lc < G && alpha != 1.f)) {
-      static_for<G>([&](auto H) {
-        const float al = read_lane(alpha, H);
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[H][e] *= al;
-      });
-    }
     if constexpr (kMasked) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -263,15 +264,52 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
         for (int j = 0; j < 4; ++j) vr[i][j] = keep ? vr[i][j] : 0u;
       }
     }
+    if constexpr (kBf16) {
+      // Rescale this lane's head column where the running max moved.
+      if (__any(lc < G && alpha != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vf[E];
-      unpack(vr[i], vf, T{});
-      static_for<G>([&](auto H) {
-        const float ph = row_bcast<H>(p[i]);
+        for (int dt = 0; dt < kDimTiles; ++dt) ot[dt] *= alpha;
+      }
+      // V tile to LDS, row-major with padded rows.
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[H][e] = fmaf(ph, vf[e], o[H][e]);
-      });
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4_t*>(vt + (4 * rg + i) * kVRow + lc * 16) = vr[i];
+      // P as two bf16 terms; lane (r, c) already holds P[4r..4r+3][c], the
+      // B operand layout of the 16x16x16 MFMA.
+      bf16x4_t phi, plo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        phi[i] = (__bf16)p[i];
+        plo[i] = (__bf16)(p[i] - (float)phi[i]);
+      }
+      const s16x4_t bhi = __builtin_bit_cast(s16x4_t, phi);
+      const s16x4_t blo = __builtin_bit_cast(s16x4_t, plo);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int dt = 0; dt < kDimTiles; ++dt) {
+        const bf16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)((__attribute__((address_space(3))) char*)vt + tr_lane + 32 * dt));
+        const s16x4_t as = __builtin_bit_cast(s16x4_t, av);
+        ot[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as, bhi, ot[dt], 0, 0, 0);
+        ot[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as, blo, ot[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      if (__any(lc < G && alpha != 1.f)) {
+        static_for<G>([&](auto H) {
+          const float al = read_lane(alpha, H);
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[H][e] *= al;
+        });
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        static_for<G>([&](auto H) {
+          const float ph = row_bcast<H>(p[i]);
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[H][e] = fmaf(ph, __uint_as_float(vr[i][e]), o[H][e]);
+        });
+      }
     }
   };
 
@@ -306,35 +344,62 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  // Sum the four row groups' shares.
+  // Sum the four row groups' shares of the softmax denominator.
   const float l_tot = sum_xor32(sum_xor16(l_run));
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[h][e] = sum_xor32(sum_xor16(o[h][e]));
 
-  static_for<G>([&](auto H) {
-    constexpr int h = H;
-    const float l_h = read_lane(l_tot, h);
-    const float m_h = read_lane(m_run, h);
-    if (rg == (h & 3)) {
-      const int64_t orow = (int64_t)s * a.q_heads + hq0 + h;
+  if constexpr (kBf16) {
+    // Lane (r, c) owns dims 16dt + 4r .. +3 of head c.
+    if (lc < G) {
+      const int64_t orow = (int64_t)s * a.q_heads + hq0 + lc;
       if (a.num_parts == 1) {
-        const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
-        store_row<E>(reinterpret_cast<T*>(a.out) + orow * D + lc * E, o[h], inv, T{});
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        __bf16* out = reinterpret_cast<__bf16*>(a.out) + orow * D + 4 * rg;
+#pragma unroll
+        for (int dt = 0; dt < kDimTiles; ++dt) {
+          bf16x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[dt][i] * inv);
+          *reinterpret_cast<bf16x4_t*>(out + 16 * dt) = w;
+        }
       } else {
         const int64_t slot = orow * a.num_parts + part;
-        float* po = a.part_o + slot * D + lc * E;
+        float* po = a.part_o + slot * D + 4 * rg;
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-          *reinterpret_cast<f32x4_t*>(po + e) = f32x4_t{o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]};
-        if (lc == 0) {
-          a.part_ml[2 * slot] = m_h;
-          a.part_ml[2 * slot + 1] = l_h;
+        for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4_t*>(po + 16 * dt) = ot[dt];
+        if (rg == 0) {
+          a.part_ml[2 * slot] = m_run;
+          a.part_ml[2 * slot + 1] = l_tot;
         }
       }
     }
-  });
+  } else {
+    // Sum the row groups' partial outputs; lanes of row group h % 4 store head h.
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[h][e] = sum_xor32(sum_xor16(o[h][e]));
+    static_for<G>([&](auto H) {
+      constexpr int h = H;
+      const float l_h = read_lane(l_tot, h);
+      const float m_h = read_lane(m_run, h);
+      if (rg == (h & 3)) {
+        const int64_t orow = (int64_t)s * a.q_heads + hq0 + h;
+        if (a.num_parts == 1) {
+          const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + orow * D + lc * E) =
+              f32x4_t{o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv};
+        } else {
+          const int64_t slot = orow * a.num_parts + part;
+          *reinterpret_cast<f32x4_t*>(a.part_o + slot * D + lc * E) =
+              f32x4_t{o[h][0], o[h][1], o[h][2], o[h][3]};
+          if (lc == 0) {
+            a.part_ml[2 * slot] = m_h;
+            a.part_ml[2 * slot + 1] = l_h;
+          }
+        }
+      }
+    });
+  }
 }
 
 // Merge of the partition states of one (sequence, query head) row:
@@ -363,12 +428,13 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
     for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[(int64_t)p * D + e], acc[e]);
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  T* out = reinterpret_cast<T*>(a.out) + (int64_t)orow * D + lane * PER;
   if constexpr (sizeof(T) == 2) {
-    static_assert(PER == 2, "bf16 reduce writes two elements per lane");
-    *reinterpret_cast<uint32_t*>(out) =
-        f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
+    static_assert(PER == 2, "bf16 merge writes two elements per lane");
+    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (int64_t)orow * D + lane * PER;
+    out[0] = (__bf16)(acc[0] * inv);
+    out[1] = (__bf16)(acc[1] * inv);
   } else {
+    float* out = reinterpret_cast<float*>(a.out) + (int64_t)orow * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = acc[e] * inv;
   }
@@ -423,6 +489,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int block
                          hipStream_t stream) {
   Launcher f = pick(dtype, head_dim, block_size, group);
   if (!f) return hipErrorInvalidValue;
+  if (a.heads_per_wg > kMaxWavesPerWg) return hipErrorInvalidValue;
   return f(a, stream);
 }
 

@@ -14,6 +14,11 @@
 
 #define PKV_EXPORT extern "C" __attribute__((visibility("default")))
 
+// Kv heads (one wave each) per decode workgroup, when kv_heads allows it.
+#ifndef PKV_DECODE_HEADS_PER_WG
+#define PKV_DECODE_HEADS_PER_WG 4
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -183,7 +188,7 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
   }
   const int group = q_heads / cache->kv_heads;
   int heads_per_wg = 1;
-  for (int w : {4, 2}) {
+  for (int w : {PKV_DECODE_HEADS_PER_WG, 4, 2}) {
     if (cache->kv_heads % w == 0) {
       heads_per_wg = w;
       break;
