@@ -41,7 +41,7 @@ def parse_args(argv=None):
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--part-tokens", type=int, default=None,
                    help="split-K partition length (default: the workload's, else the library's)")
-    p.add_argument("--cpu-sample", type=int, default=128,
+    p.add_argument("--cpu-sample", type=int, default=256,
                    help="sequences the oracle computes for the CPU baseline (0 skips it)")
     p.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                    help="instead of the decode step, time a plain device-to-device copy of "
@@ -72,6 +72,30 @@ def copy_probe(gib, steps, warmup):
     return 0
 
 
+PROFILE = os.path.join(ROOT, "profiles", "paged_attn_decode_c3_gqa4k_bf16.md")
+DECODE_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_decode.hip",
+                  "paged_kv_cache_317_amd/csrc/device_common.hpp",
+                  "paged_kv_cache_317_amd/csrc/kernels.hpp"]
+
+
+def profiled_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none for this workload or the kernel sources changed since."""
+    import hashlib
+    import re
+    if workload != DEFAULT_WORKLOAD or not os.path.exists(PROFILE):
+        return None
+    text = open(PROFILE).read()
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    traffic = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not sha or not traffic:
+        return None
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return int(traffic.group(1)) if h.hexdigest() == sha.group(1) else None
+
+
 def step_bytes(cfg, lens):
     """Algorithmic bytes of one decode launch and of one slot-write launch."""
     import numpy as np
@@ -83,7 +107,9 @@ def step_bytes(cfg, lens):
     tables = int(blocks.sum()) * 4 + cfg.num_seqs * 4
     decode = kv + qo + tables
     write = cfg.num_seqs * (cfg.kv_heads * cfg.head_dim * e * 2 * 2 + 8)
-    return {"decode": decode, "kv_read": kv, "kv_write": write}
+    repeat = (cfg.num_seqs - 1) * cfg.prefix_tokens * cfg.kv_heads * cfg.head_dim * e * 2
+    return {"decode": decode, "kv_read": kv, "kv_write": write,
+            "shared_repeat": repeat if cfg.prefix_tokens else 0}
 
 
 def host_array(t):
@@ -120,6 +146,51 @@ def cpu_baseline(cfg, q, k_cache, v_cache, table, lens, nseq):
         "sample": f"first {nseq} of {cfg.num_seqs} sequences of the same batch (same pools), "
                   f"one decode step, fp64 numpy, BLAS limited to 1 thread",
     }
+
+
+def time_cache_ops(pkv, w, cfg, dev, per_graph=100, replays=5):
+    """Slot write (one token per sequence) and a copy-on-write sized block
+    copy (one block per sequence but the last, free source and destination
+    blocks), each timed on its own.  The launches are captured in a HIP graph
+    so that the figure is device time, not the host's launch rate; bytes are
+    read + written."""
+    import numpy as np
+    import torch
+    lay = w.layout
+    res = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (replays * per_graph)
+
+    row = cfg.kv_heads * cfg.head_dim * cfg.elem_bytes
+    ms = timed(lambda: pkv.paged_kv_write(w.new_k, w.new_v, w.slot_mapping, w.k_cache, w.v_cache))
+    nbytes = cfg.num_seqs * (row * 2 * 2 + 8)
+    res["paged_kv_write"] = {"tokens": cfg.num_seqs, "us": round(ms * 1e3, 3),
+                             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    npairs = min(cfg.num_seqs - 1, lay.spare_blocks.size // 2)
+    if npairs > 0:
+        src = lay.spare_blocks[:npairs]
+        dst = lay.spare_blocks[npairs:2 * npairs]
+        pairs = torch.from_numpy(np.stack([src, dst], axis=1).astype(np.int64)).to(dev)
+        ms = timed(lambda: pkv.paged_block_copy(pairs, w.k_cache, w.v_cache))
+        nbytes = npairs * row * cfg.block_size * 2 * 2
+        res["paged_block_copy"] = {"pairs": int(npairs), "us": round(ms * 1e3, 3),
+                                   "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return res
 
 
 def main(argv=None):
@@ -192,7 +263,13 @@ def main(argv=None):
     nb = step_bytes(cfg, lay.seq_lens)
     step_total = nb["decode"] + nb["kv_write"]
     value = step_total / (step_ms * 1e-3) / 1e9
-    achieved = nb["decode"] / (decode_ms * 1e-3) / 1e9
+    # HBM has to deliver each stored row once: with a shared prefix the
+    # roofline counts the prefix once (the effective figure counts it per
+    # sequence).
+    roof_bytes = nb["decode"] - nb["shared_repeat"]
+    achieved = roof_bytes / (decode_ms * 1e-3) / 1e9
+
+    ops = time_cache_ops(pkv, w, cfg, dev)
 
     cpu = None
     if args.cpu_sample > 0:
@@ -236,11 +313,15 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": nb["decode"],
-            "traffic": None,
+            "bytes_per_launch": roof_bytes,
+            "traffic": profiled_traffic(cfg.name),
         },
         "cpu_baseline": cpu,
+        "ops": ops,
     }
+    if cfg.prefix_tokens:
+        line["unique_bytes_per_launch"] = roof_bytes
+        line["effective_decode_GBps"] = round(nb["decode"] / (decode_ms * 1e-3) / 1e9, 2)
     print(json.dumps(line), flush=True)
     return 0
 

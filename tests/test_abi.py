@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports what include/pkv.h
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_317_amd as pkv
+from paged_kv_cache_317_amd._lib import CacheDesc, SIGNATURES, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib(), name) is not None
+    # nothing else leaks out of the C ABI
+    assert {n for n in exported if n.startswith("pkv")} == set(declared_functions())
+
+
+def test_version_string():
+    assert lib().pkv_version().decode().startswith("pkv ")
+
+
+def _desc(nb=64, bs=16, hkv=8, d=128, dtype=1):
+    return CacheDesc(nb, bs, hkv, d, dtype)
+
+
+def _decode(desc, S=2, Hq=32, max_len=100, part=0, q=1 << 12, kc=1 << 12, vc=1 << 12,
+            table=1 << 12, lens=1 << 12, out=1 << 12, ws=None, ws_bytes=0, width=8):
+    return lib().pkv_paged_attn_decode(q, kc, vc, ctypes.byref(desc) if desc else None, table,
+                                       width, lens, S, Hq, max_len, 0.1, out, part, ws, ws_bytes,
+                                       None)
+
+
+def _status(code):
+    return {0: "OK", 1: "NULL", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED", 5: "WORKSPACE",
+            6: "HIP", 7: "ALIGN"}[code]
+
+
+def test_decode_argument_checks_run_before_any_launch():
+    assert _status(_decode(None)) == "NULL"
+    assert _status(_decode(_desc(dtype=9))) == "DTYPE"
+    assert _status(_decode(_desc(), Hq=30)) == "SHAPE"               # not a multiple of 8
+    assert _status(_decode(_desc(d=96))) == "UNSUPPORTED"
+    assert _status(_decode(_desc(bs=8))) == "UNSUPPORTED"
+    assert _status(_decode(_desc(), Hq=8 * 16)) == "UNSUPPORTED"     # group 16 not built
+    assert _status(_decode(_desc(nb=0))) == "SHAPE"
+    assert _status(_decode(_desc(), q=0)) == "NULL"
+    assert _status(_decode(_desc(), q=(1 << 12) + 2)) == "ALIGN"
+    assert _status(_decode(_desc(), width=0)) == "SHAPE"
+    assert _status(_decode(_desc(), S=-1)) == "SHAPE"
+    assert "q_heads" in lib().pkv_last_error().decode() or lib().pkv_last_error()
+    # a split call without a workspace
+    assert _status(_decode(_desc(), max_len=4096, part=512)) == "WORKSPACE"
+    assert "workspace" in lib().pkv_last_error().decode()
+    # zero sequences: nothing to launch, OK even with NULL pointers
+    assert _status(_decode(_desc(), S=0, q=0, kc=0, vc=0, table=0, lens=0, out=0)) == "OK"
+    assert lib().pkv_last_error() == b""
+
+
+def test_kv_write_and_block_copy_argument_checks():
+    L = lib()
+    d = _desc()
+    assert _status(L.pkv_paged_kv_write(1 << 12, 1 << 12, 1 << 12, 4, 1 << 12, 1 << 12, None,
+                                        None)) == "NULL"
+    assert _status(L.pkv_paged_kv_write(0, 1 << 12, 1 << 12, 4, 1 << 12, 1 << 12,
+                                        ctypes.byref(d), None)) == "NULL"
+    assert _status(L.pkv_paged_kv_write(1 << 12, 1 << 12, 1 << 12, -1, 1 << 12, 1 << 12,
+                                        ctypes.byref(d), None)) == "SHAPE"
+    assert _status(L.pkv_paged_kv_write(None, None, None, 0, None, None, ctypes.byref(d),
+                                        None)) == "OK"
+    assert _status(L.pkv_paged_kv_write((1 << 12) + 8, 1 << 12, 1 << 12, 4, 1 << 12, 1 << 12,
+                                        ctypes.byref(d), None)) == "ALIGN"
+    assert _status(L.pkv_paged_block_copy(None, 3, 1 << 12, 1 << 12, ctypes.byref(d),
+                                          None)) == "NULL"
+    assert _status(L.pkv_paged_block_copy(1 << 12, -2, 1 << 12, 1 << 12, ctypes.byref(d),
+                                          None)) == "SHAPE"
+    assert _status(L.pkv_paged_block_copy(None, 0, None, None, ctypes.byref(d), None)) == "OK"
+    odd = _desc(d=60, dtype=1)                        # 120-byte rows: not 16-byte multiples
+    assert _status(L.pkv_paged_block_copy(1 << 12, 1, 1 << 12, 1 << 12, ctypes.byref(odd),
+                                          None)) == "UNSUPPORTED"
+
+
+@pytest.mark.parametrize("S,Hkv,max_len,req,expect", [
+    (256, 8, 4096, 0, 4096),      # enough waves: unsplit
+    (16, 8, 131072, 0, 8192),     # few sequences: split until 2048 waves
+    (16, 8, 131072, 512, 512),    # explicit request
+    (4, 8, 100, 0, 112),          # one partition of the rounded-up length
+    (2, 8, 1_000_000, 0, 4096),   # capped by the LDS table slice, then halved to 2048+ waves
+])
+def test_partition_choice(S, Hkv, max_len, req, expect):
+    d = _desc(hkv=Hkv)
+    got = lib().pkv_decode_partition_tokens(ctypes.byref(d), S, Hkv * 4, max_len, req)
+    assert got == expect
+    ws = lib().pkv_decode_workspace_size(ctypes.byref(d), S, Hkv * 4, max_len, req)
+    P = -(-max_len // got)
+    rows = S * Hkv * 4 * P
+    assert ws == (0 if P == 1 else (-(-2 * rows // 4) * 4 + rows * 128) * 4)
+
+
+def test_partition_request_rounds_to_block_size():
+    d = _desc(bs=32)
+    assert lib().pkv_decode_partition_tokens(ctypes.byref(d), 4, 32, 10_000, 100) == 128

@@ -105,3 +105,44 @@ def test_block_copy_zero_pairs_is_a_noop():
                          d["k_cache"], d["v_cache"])
     torch.cuda.synchronize()
     assert np.array_equal(to_host(d["k_cache"], "f32"), w.k_cache)
+
+
+def test_ops_replay_correctly_inside_a_captured_graph():
+    """Slot write, decode and block copy captured in one HIP graph, replayed
+    several times with eager work in between; every replay matches eager."""
+    cfg = scaled(get_config("c5_long_bf16"), num_seqs=3, len_range=(600, 1500), max_len=1536,
+                 part_tokens=256)
+    w = generate_host(cfg)
+    d = upload(w)
+    lay = w.layout
+    pairs = torch.from_numpy(np.stack([lay.spare_blocks[:2], lay.spare_blocks[2:4]], 1)
+                             .astype(np.int64)).cuda()
+    out = torch.empty_like(d["q"])
+    ws = torch.empty(pkv.decode_workspace_size(d["k_cache"], cfg.num_seqs, cfg.q_heads,
+                                               lay.max_seq_len, cfg.part_tokens),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        pkv.paged_kv_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+        pkv.paged_block_copy(pairs, d["k_cache"], d["v_cache"])
+        pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["seq_lens"],
+                              cfg.scale, lay.max_seq_len, out=out, part_tokens=cfg.part_tokens,
+                              workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    eager_k, eager_v = d["k_cache"].clone(), d["v_cache"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        d["k_cache"].copy_(to_device(w.k_cache, "bf16"))
+        d["v_cache"].copy_(to_device(w.v_cache, "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager_out.view(torch.int16)), f"replay {r}"
+        assert torch.equal(d["k_cache"].view(torch.int16), eager_k.view(torch.int16))
+        assert torch.equal(d["v_cache"].view(torch.int16), eager_v.view(torch.int16))
