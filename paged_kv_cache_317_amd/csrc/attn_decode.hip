@@ -114,8 +114,14 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_s
 
 // Occupancy request: waves per SIMD the register allocation must allow.
 #ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 2
+#define PKV_DECODE_WAVES_PER_EU 4
 #endif
+// Tiles in flight per wave while one is computed (register sets: 1 or 2).
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 1
+#endif
+constexpr int kDepth = PKV_DECODE_DEPTH;
+static_assert(kDepth == 1 || kDepth == 2, "one or two register sets");
 
 template <typename T, int D, int BS, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
@@ -264,32 +270,53 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // One tile: logits, online-softmax update, P.V.  kMasked handles the one
-  // ragged tile at the end of a partition: tokens at or past t1 get weight 0
-  // and their value rows (unused slots, any bits) are replaced by zeros.
-  auto process = [&](auto masked, int tile, const u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int tb = t0 + tile * kTile;
-    f32x4_t acc;
-    if constexpr (kBf16) {
-      // K rows to LDS as loaded, then back in the operand layout.
+  // One tile, with its K and V rows in registers as loaded.  `tb` is the
+  // tile's first position; tokens at or past t1 get weight 0 (only the last
+  // tile of a partition can hold such tokens, `ragged`), and their value rows
+  // (unused slots, any bits) are replaced by zeros.
+  //
+  // bf16: the rows are staged in LDS first, then `next` (the loads of the
+  // following tile into the same registers) is issued, so one register set
+  // serves both the tile in flight and the tile being computed.
+  auto process = [&](int tb, bool ragged, u32x4_t (&kr)[4], u32x4_t (&vr)[4], auto&& next) {
+    if (ragged) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const bool keep = tb + 4 * rg + i < t1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vr[i][j] = keep ? vr[i][j] : 0u;
+      }
+    }
+    f32x4_t acc;
+    u32x4_t vkeep[kBf16 ? 1 : 4];
+    if constexpr (kBf16) {
+      // K and V rows to LDS as loaded (padded rows), then the next loads.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         *reinterpret_cast<u32x4_t*>(kt + (4 * rg + i) * kKRow + lc * 16) = kr[i];
+        *reinterpret_cast<u32x4_t*>(vt + (4 * rg + i) * kVRow + lc * 16) = vr[i];
+      }
+      next();
       __builtin_amdgcn_wave_barrier();
       u32x4_t ka[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) ka[c] = *reinterpret_cast<const u32x4_t*>(kt + ka_lane + 64 * c);
-      __builtin_amdgcn_wave_barrier();
       acc = tile_logits(ka, qv, T{});
     } else {
-      acc = tile_logits(kr, qv, T{});
+      u32x4_t kc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kc[i] = kr[i];
+        vkeep[i] = vr[i];
+      }
+      next();
+      acc = tile_logits(kc, qv, T{});
     }
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = acc[i] * a.scale_log2;
-      if (kMasked && tb + 4 * rg + i >= t1) x[i] = -INFINITY;
+      if (tb + 4 * rg + i >= t1) x[i] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_xor32(max_xor16(mx));
@@ -301,24 +328,12 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
     l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;
-    if constexpr (kMasked) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool keep = tb + 4 * rg + i < t1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vr[i][j] = keep ? vr[i][j] : 0u;
-      }
-    }
     if constexpr (kBf16) {
       // Rescale this lane's head column where the running max moved.
       if (__any(lc < G && alpha != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < kDimTiles; ++dt) ot[dt] *= alpha;
       }
-      // V tile to LDS, row-major with padded rows.
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t*>(vt + (4 * rg + i) * kVRow + lc * 16) = vr[i];
       // P as two bf16 terms; lane (r, c) already holds P[4r..4r+3][c], the
       // B operand layout of the 16x16x16 MFMA.
       bf16x4_t phi, plo;
@@ -329,7 +344,6 @@ void decode_partition_kernel(DecodeArgs a) {
       }
       const s16x4_t bhi = __builtin_bit_cast(s16x4_t, phi);
       const s16x4_t blo = __builtin_bit_cast(s16x4_t, plo);
-      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int dt = 0; dt < kDimTiles; ++dt) {
         const bf16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -352,40 +366,35 @@ void decode_partition_kernel(DecodeArgs a) {
         static_for<G>([&](auto H) {
           const float ph = row_bcast<H>(p[i]);
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[H][e] = fmaf(ph, __uint_as_float(vr[i][e]), o[H][e]);
+          for (int e = 0; e < E; ++e) o[H][e] = fmaf(ph, __uint_as_float(vkeep[i][e]), o[H][e]);
         });
       }
     }
   };
 
-  // Two register sets, refilled as soon as they are consumed: while one tile
-  // is computed the next is in flight.  Tiles 0 .. nfull-1 are full; a
-  // ragged tile, if any, is the last one and goes through the masked path.
-  // Loads past the last tile re-read it (an L2 hit) so that every iteration
-  // issues the same loads.
+  // kDepth register sets, each refilled as soon as its tile is staged: while
+  // tile t is computed, tiles t+1 .. t+kDepth are in flight.  Loads past the
+  // last tile re-read it (an L2 hit) so that every iteration issues the same
+  // loads.
   const int ntiles = (ntok + kTile - 1) / kTile;
   const int nfull = ntok / kTile;
   if (ntiles > 0) {
-    const std::false_type full{};
-    const std::true_type ragged{};
-    u32x4_t ka[4], va[4], kb[4], vb[4];
-    load_tile(0, ka, va);
-    load_tile(min(1, ntiles - 1), kb, vb);
-    for (int t = 0;; t += 2) {
-      if (t == nfull) {
-        process(ragged, t, ka, va);
-        break;
+    const int last = ntiles - 1;
+    if constexpr (kDepth == 1) {
+      u32x4_t kr[4], vr[4];
+      load_tile(0, kr, vr);
+      for (int t = 0; t < ntiles; ++t)
+        process(t0 + t * kTile, t == nfull, kr, vr, [&] { load_tile(min(t + 1, last), kr, vr); });
+    } else {
+      u32x4_t ka[4], va[4], kb[4], vb[4];
+      load_tile(0, ka, va);
+      load_tile(min(1, last), kb, vb);
+      for (int t = 0; t < ntiles; t += 2) {
+        process(t0 + t * kTile, t == nfull, ka, va, [&] { load_tile(min(t + 2, last), ka, va); });
+        if (t + 1 >= ntiles) break;
+        process(t0 + (t + 1) * kTile, t + 1 == nfull, kb, vb,
+                [&] { load_tile(min(t + 3, last), kb, vb); });
       }
-      process(full, t, ka, va);
-      if (t + 1 >= ntiles) break;
-      load_tile(min(t + 2, ntiles - 1), ka, va);
-      if (t + 1 == nfull) {
-        process(ragged, t + 1, kb, vb);
-        break;
-      }
-      process(full, t + 1, kb, vb);
-      if (t + 2 >= ntiles) break;
-      load_tile(min(t + 3, ntiles - 1), kb, vb);
     }
   }
 
