@@ -66,7 +66,9 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 4, /* well-formed, but no kernel is built for it     */
   PKV_ERR_WORKSPACE = 5,   /* split decode needs a (larger) workspace        */
   PKV_ERR_HIP = 6,         /* the HIP runtime rejected a launch              */
-  PKV_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned               */
+  PKV_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned               */
+  PKV_ERR_NO_BLOCKS = 8,   /* block manager: the pool has too few free blocks */
+  PKV_ERR_KEY = 9          /* block manager: unknown or duplicate sequence id */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -175,6 +177,103 @@ size_t pkv_decode_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
 pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pairs,
                                 void* k_cache, void* v_cache,
                                 const pkv_cache_desc* cache, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block manager (host memory only; no device work, no stream).
+ *
+ * Owns the bookkeeping of one pool: which physical blocks are free, each
+ * block's reference count and filled slots, and each sequence's block table
+ * and length.  It implements the pages' allocation rules:
+ *   - a sequence of L tokens holds ceil(L / block_size) blocks, all full but
+ *     the last ("PagedAttention Explained", "How PagedAttention works",
+ *     steps 1-2; "What does PagedAttention change in LLM KV allocation?",
+ *     "Calculate unused block space");
+ *   - a new block is taken only when the sequence's last block is full,
+ *     nothing is reserved ahead (same page, step 4), and blocks return to
+ *     the pool when no sequence references them any more;
+ *   - sequences may share blocks (fork); a sequence about to write into a
+ *     block with reference count > 1 first gets a copy, reported as a
+ *     (src, dst) pair for pkv_paged_block_copy, and its table then points at
+ *     the copy; the last holder writes in place ("Sharing blocks between
+ *     sequences").
+ * Every call validates its arguments and either succeeds completely or
+ * changes nothing.  A manager is not thread-safe; use one per thread or
+ * lock around it.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* Counters of one pool (the measurements "What does PagedAttention change in
+ * LLM KV allocation?", "Sharing requires more than allocation", asks for). */
+typedef struct {
+  int64_t allocated_blocks; /* blocks with reference count > 0               */
+  int64_t allocated_slots;  /* allocated_blocks * block_size                 */
+  int64_t used_slots;       /* token positions stored, a shared block once   */
+  int64_t free_blocks;
+  int64_t sequences;        /* live sequences                                */
+  int64_t logical_tokens;   /* sum of live sequence lengths                  */
+  int64_t copies;           /* copy-on-write pairs handed out so far         */
+  int64_t preemptions;      /* sequences released by pkv_bm_preempt so far   */
+} pkv_bm_stats;
+
+/* Create a manager for num_blocks blocks of block_size slots.  free_order
+ * (host, num_blocks entries, a permutation of 0..num_blocks-1) sets the
+ * order in which free blocks are handed out; NULL means ascending ids.
+ * Released blocks go to the back of the free list. */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* free_order, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Start an empty sequence under a new id. */
+pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq);
+
+/* Start `child` as a copy of `parent` that shares all of its blocks
+ * (reference counts + 1); used for parallel samples, beams and shared
+ * prompt prefixes ("Sharing blocks between sequences"). */
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Store n new tokens of `seq`.  slots (host, n entries) receives each new
+ * token's slot (physical_block * block_size + offset) for
+ * pkv_paged_kv_write; copies (host, copies_cap x 2) receives the (src, dst)
+ * block copies the writes need, in order, and *n_copies their number (at
+ * most one per call).  Fails with PKV_ERR_NO_BLOCKS, changing nothing, when
+ * the pool cannot supply the blocks the call needs. */
+pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t n,
+                         int64_t* slots, int64_t* copies, int32_t copies_cap,
+                         int32_t* n_copies);
+
+/* Blocks pkv_bm_append(seq, n) would take from the pool (new blocks plus a
+ * copy-on-write copy if the last block is shared and not full). */
+pkv_status pkv_bm_blocks_needed(const pkv_block_manager* bm, int64_t seq,
+                                int32_t n, int32_t* blocks);
+
+/* Release a finished sequence; blocks nobody references return to the pool. */
+pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq);
+
+/* Release a sequence the scheduler preempts (its cache is dropped, to be
+ * recomputed or restored later; "PagedAttention Explained", "Preemption and
+ * scheduling"); counted in pkv_bm_stats.preemptions. */
+pkv_status pkv_bm_preempt(pkv_block_manager* bm, int64_t seq);
+
+/* Length (tokens) of a sequence. */
+pkv_status pkv_bm_length(const pkv_block_manager* bm, int64_t seq, int32_t* len);
+
+/* Block tables of n sequences as int32 [n, width] in host memory, entries
+ * past each sequence's blocks set to -1; PKV_ERR_SHAPE if a sequence holds
+ * more than width blocks. */
+pkv_status pkv_bm_table(const pkv_block_manager* bm, const int64_t* seqs,
+                        int32_t n, int32_t width, int32_t* table);
+
+pkv_status pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats* out);
+
+/* Capacity of a pool for a list of request lengths taken in order:
+ * *paged = how many leading requests fit when each takes ceil(len /
+ * block_size) blocks; *contiguous = how many fit when each reserves
+ * reserve_len token slots up front (the scheme paged blocks replace,
+ * "PagedAttention Explained", table "Contiguous allocation vs
+ * PagedAttention").  Lengths above reserve_len are an error. */
+pkv_status pkv_capacity(int64_t num_blocks, int32_t block_size,
+                        const int32_t* lens, int32_t n, int32_t reserve_len,
+                        int32_t* paged, int32_t* contiguous);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);

@@ -11,6 +11,7 @@ PKV_F32, PKV_BF16 = 0, 1
 STATUS_NAMES = {
     0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_DTYPE",
     4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP", 7: "PKV_ERR_ALIGN",
+    8: "PKV_ERR_NO_BLOCKS", 9: "PKV_ERR_KEY",
 }
 
 
@@ -25,6 +26,13 @@ class CacheDesc(ctypes.Structure):
     ]
 
 
+class BmStats(ctypes.Structure):
+    """Mirror of ``pkv_bm_stats``."""
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "allocated_blocks", "allocated_slots", "used_slots", "free_blocks", "sequences",
+        "logical_tokens", "copies", "preemptions")]
+
+
 class PkvError(RuntimeError):
     """A non-OK ``pkv_status``, with the library's message."""
 
@@ -37,6 +45,7 @@ class PkvError(RuntimeError):
 _vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                               ctypes.c_float, ctypes.c_size_t)
 _desc = ctypes.POINTER(CacheDesc)
+_p = ctypes.POINTER
 
 SIGNATURES = {
     "pkv_paged_kv_write": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _desc, _vp]),
@@ -45,6 +54,18 @@ SIGNATURES = {
     "pkv_decode_partition_tokens": (_i32, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_decode_workspace_size": (_sz, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_paged_block_copy": (_i32, [_vp, _i32, _vp, _vp, _desc, _vp]),
+    "pkv_bm_create": (_i32, [_i32, _i32, _vp, _p(_vp)]),
+    "pkv_bm_destroy": (None, [_vp]),
+    "pkv_bm_add": (_i32, [_vp, _i64]),
+    "pkv_bm_fork": (_i32, [_vp, _i64, _i64]),
+    "pkv_bm_append": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _p(_i32)]),
+    "pkv_bm_blocks_needed": (_i32, [_vp, _i64, _i32, _p(_i32)]),
+    "pkv_bm_free": (_i32, [_vp, _i64]),
+    "pkv_bm_preempt": (_i32, [_vp, _i64]),
+    "pkv_bm_length": (_i32, [_vp, _i64, _p(_i32)]),
+    "pkv_bm_table": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "pkv_bm_get_stats": (_i32, [_vp, _p(BmStats)]),
+    "pkv_capacity": (_i32, [_i64, _i32, _vp, _i32, _i32, _p(_i32), _p(_i32)]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }

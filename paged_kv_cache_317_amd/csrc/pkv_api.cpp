@@ -11,17 +11,21 @@
 
 #include "../../include/pkv.h"
 #include "kernels.hpp"
+#include "status.hpp"
 
-#define PKV_EXPORT extern "C" __attribute__((visibility("default")))
+namespace pkv {
+const char* last_error();
+}
 
 // Kv heads (one wave each) per decode workgroup, when kv_heads allows it.
 #ifndef PKV_DECODE_HEADS_PER_WG
 #define PKV_DECODE_HEADS_PER_WG 4
 #endif
 
+namespace pkv {
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
 pkv_status fail(pkv_status st, const char* fmt, ...) {
   char buf[512];
@@ -37,6 +41,15 @@ pkv_status ok() {
   g_last_error.clear();
   return PKV_OK;
 }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+using pkv::ok;
 
 pkv_status from_hip(hipError_t err, const char* what) {
   if (err == hipSuccess) return ok();
@@ -116,7 +129,7 @@ pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_head
 
 }  // namespace
 
-PKV_EXPORT const char* pkv_last_error(void) { return g_last_error.c_str(); }
+PKV_EXPORT const char* pkv_last_error(void) { return pkv::last_error(); }
 
 PKV_EXPORT const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
 

@@ -1,0 +1,216 @@
+"""The native host block manager (libpkv, pkv_bm_*) against the oracle's.
+
+Host logic, no GPU: the same operations with the same free-block order must
+give the same slots, copy pairs, block tables and counters.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.block_manager import BlockManager as OracleBM, OutOfBlocks, blocks_for
+from paged_kv_cache_317_amd.block_manager import BlockManager, PkvError, capacity
+from workloads import build_layout, cow_layout, get_config
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _same_state(nat, orc, live, width):
+    ids = sorted(live)
+    if ids:
+        assert np.array_equal(nat.table_array(ids, width), orc.table_array(ids, width))
+        for s in ids:
+            assert nat.length(s) == orc.lengths[s]
+    a, b = nat.stats(), orc.stats()
+    for k in ("allocated_blocks", "allocated_slots", "used_slots", "unused_slots",
+              "free_blocks", "sequences"):
+        assert a[k] == b[k], k
+    assert a["logical_tokens"] == sum(orc.lengths.values())
+
+
+def test_worked_example_35_tokens():
+    fx = json.load(open(os.path.join(GOLDEN, "worked_example_35_tokens.json")))
+    bm = BlockManager(8, fx["block_size"])
+    bm.add(0)
+    bm.append(0, fx["tokens"])
+    st = bm.stats()
+    assert st["allocated_blocks"] == fx["blocks"]
+    assert st["allocated_slots"] == fx["slots"]
+    assert st["unused_slots"] == fx["unused_slots"]
+    assert round(st["waste_fraction"], 2) == fx["unused_fraction_approx"]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_operations_match_the_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    NB = int(rng.integers(20, 120))
+    BS = int(rng.choice([1, 4, 16, 32]))
+    order = rng.permutation(NB)
+    nat, orc = BlockManager(NB, BS, free_order=order), OracleBM(NB, BS, free_order=order)
+    live, next_id, width = set(), 0, NB
+    for step in range(300):
+        op = rng.choice(["add", "fork", "append", "append", "append", "free", "preempt"])
+        if op == "add" or not live:
+            nat.add(next_id)
+            orc.add(next_id)
+            live.add(next_id)
+            next_id += 1
+        elif op == "fork":
+            parent = int(rng.choice(sorted(live)))
+            nat.fork(parent, next_id)
+            orc.fork(parent, next_id)
+            live.add(next_id)
+            next_id += 1
+        elif op == "append":
+            s = int(rng.choice(sorted(live)))
+            n = int(rng.integers(0, 3 * BS + 2))
+            need = nat.blocks_needed(s, n)
+            before = nat.stats()
+            if need > len(orc.free):
+                with pytest.raises(PkvError) as e:
+                    nat.append(s, n)
+                assert e.value.status_name == "PKV_ERR_NO_BLOCKS"
+                assert nat.stats() == before          # nothing changed
+                continue
+            got = nat.append(s, n)
+            ref = orc.append(s, n)
+            assert got == ref
+            assert nat.stats()["allocated_blocks"] - before["allocated_blocks"] <= need
+            assert before["free_blocks"] - nat.stats()["free_blocks"] == need
+        else:
+            s = int(rng.choice(sorted(live)))
+            (nat.preempt if op == "preempt" else nat.free_sequence)(s)
+            orc.free_sequence(s)
+            live.discard(s)
+        _same_state(nat, orc, live, width)
+
+
+def test_copy_on_write_and_last_holder():
+    bm = BlockManager(16, 4)
+    bm.add(0)
+    bm.append(0, 10)                 # blocks 0,1 full, block 2 holds 2 tokens
+    bm.fork(0, 1)
+    bm.fork(0, 2)
+    assert bm.blocks_needed(1, 1) == 1
+    slots, copies = bm.append(1, 1)
+    assert copies == [(2, 3)] and slots == [3 * 4 + 2]
+    _, copies = bm.append(2, 1)
+    assert copies == [(2, 4)]
+    assert bm.blocks_needed(0, 1) == 0
+    _, copies = bm.append(0, 1)      # last holder writes in place
+    assert copies == []
+    assert bm.stats()["copies"] == 2
+
+
+def test_free_and_preempt_counters():
+    bm = BlockManager(8, 4)
+    bm.add(0)
+    bm.append(0, 8)
+    bm.fork(0, 1)
+    bm.append(1, 1)
+    bm.preempt(0)
+    st = bm.stats()
+    assert st["preemptions"] == 1 and st["allocated_blocks"] == 3
+    bm.free_sequence(1)
+    assert bm.stats()["allocated_blocks"] == 0 and bm.stats()["free_blocks"] == 8
+
+
+def test_errors_change_nothing():
+    bm = BlockManager(4, 4)
+    bm.add(7)
+    with pytest.raises(PkvError) as e:
+        bm.add(7)
+    assert e.value.status_name == "PKV_ERR_KEY"
+    with pytest.raises(PkvError) as e:
+        bm.append(8, 1)
+    assert e.value.status_name == "PKV_ERR_KEY"
+    bm.append(7, 12)
+    before = bm.stats()
+    with pytest.raises(PkvError) as e:
+        bm.append(7, 5)                           # needs 2 blocks, 1 free
+    assert e.value.status_name == "PKV_ERR_NO_BLOCKS"
+    assert bm.stats() == before and bm.length(7) == 12
+    with pytest.raises(PkvError) as e:
+        bm.table_array([7], 2)                    # 3 blocks > width 2
+    assert e.value.status_name == "PKV_ERR_SHAPE"
+    with pytest.raises(PkvError):
+        BlockManager(4, 4, free_order=[0, 1, 1, 2])
+
+
+def test_oracle_raises_where_the_native_manager_refuses():
+    orc, nat = OracleBM(2, 4), BlockManager(2, 4)
+    for bm in (orc, nat):
+        bm.add(0)
+        bm.append(0, 8)
+    with pytest.raises(OutOfBlocks):
+        orc.append(0, 1)
+    with pytest.raises(PkvError):
+        nat.append(0, 1)
+
+
+def test_c4_layout_replays_exactly():
+    cfg = get_config("c4_prefix_bf16")
+    lay = build_layout(cfg)
+    order = list(lay.shared_blocks) + [int(b) for b in lay.block_table[:, 64:].ravel() if b >= 0]
+    order += list(lay.spare_blocks)
+    bm = BlockManager(lay.num_blocks, cfg.block_size, free_order=order)
+    bm.add(0)
+    bm.append(0, cfg.prefix_tokens)
+    for s in range(1, cfg.num_seqs):
+        bm.fork(0, s)
+    for s in range(cfg.num_seqs):
+        _, copies = bm.append(s, int(lay.seq_lens[s]) - cfg.prefix_tokens)
+        assert copies == []
+    assert np.array_equal(bm.table_array(range(cfg.num_seqs), cfg.table_width), lay.block_table)
+
+
+def test_cow_scenario_pairs_match_the_workload():
+    cfg = get_config("c4_prefix_bf16")
+    lay = build_layout(cfg)
+    sc = cow_layout(lay, 1016)
+    nshared = -(-1016 // cfg.block_size)
+    order = list(lay.shared_blocks[:nshared]) + list(lay.spare_blocks)
+    order += [b for b in range(lay.num_blocks) if b not in set(order)]
+    bm = BlockManager(lay.num_blocks, cfg.block_size, free_order=order)
+    S = cfg.num_seqs
+    bm.add(S - 1)
+    bm.append(S - 1, 1016)
+    for s in range(S - 1):
+        bm.fork(S - 1, s)
+    pairs, slots = [], []
+    for s in range(S):
+        sl, cp = bm.append(s, 1)
+        pairs += cp
+        slots += sl
+    assert np.array_equal(np.array(pairs), sc["pairs"])
+    assert np.array_equal(np.array(slots), sc["write_slots"])
+    assert bm.stats()["copies"] == S - 1
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_capacity_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    NB, BS, R = int(rng.integers(1, 400)), int(rng.choice([8, 16, 32])), 2048
+    lens = rng.integers(0, R + 1, size=int(rng.integers(0, 60)))
+    paged, contig = capacity(NB, BS, lens, R)
+    used, fit = 0, 0
+    for L in lens:
+        used += blocks_for(int(L), BS)
+        if used > NB:
+            break
+        fit += 1
+    assert paged == fit
+    assert contig == min(len(lens), NB * BS // R)
+
+
+def test_capacity_on_a_serving_like_mix():
+    """With lengths U{1..2048} a request holds ~1045 slots on average instead of
+    a 2048-slot reservation, so about 1.96x as many requests fit."""
+    rng = np.random.default_rng(9)
+    lens = rng.integers(1, 2049, size=4000)
+    paged, contig = capacity(20_000, 16, lens, 2048)
+    assert contig == 20_000 * 16 // 2048
+    held = (-(-lens // 16) * 16)[:paged].mean()
+    assert abs(paged / contig - 2048 / held) < 0.05
