@@ -193,6 +193,65 @@ def time_cache_ops(pkv, w, cfg, dev, per_graph=100, replays=5):
     return res
 
 
+def allocator_report(cfg, lay):
+    """The batch's tables built through the native block manager (a shared
+    prefix by fork), then one decode step of one-token appends; then the
+    same pool filled with more sequences of the batch's lengths until the
+    manager refuses (the concurrent capacity), against a max-length
+    reservation of the same pool."""
+    import numpy as np
+    from paged_kv_cache_317_amd.block_manager import BlockManager, PkvError
+    BS, S = cfg.block_size, cfg.num_seqs
+    lens = lay.seq_lens.astype(np.int64)
+    pre = cfg.prefix_tokens
+
+    def populate(bm, count):
+        """Add `count` sequences (lengths cycle through the batch); returns how
+        many fit and the appended token count."""
+        tokens = 0
+        if pre:
+            bm.add(-1)
+            bm.append(-1, pre)
+        for i in range(count):
+            L = int(lens[i % S])
+            try:
+                if pre:
+                    bm.fork(-1, i)
+                    bm.append(i, L - pre)
+                    tokens += L - pre
+                else:
+                    bm.add(i)
+                    bm.append(i, L)
+                    tokens += L
+            except PkvError as e:
+                if e.status_name != "PKV_ERR_NO_BLOCKS":
+                    raise
+                bm.free_sequence(i)
+                return i, tokens
+        return count, tokens
+
+    bm = BlockManager(lay.num_blocks, BS)
+    t0 = time.perf_counter()
+    _, tokens = populate(bm, S)
+    t_bulk = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(S):
+        bm.append(i, 1)
+    t_step = time.perf_counter() - t0
+    st = bm.stats()
+    cap, _ = populate(BlockManager(lay.num_blocks, BS), 1 << 30)
+    return {
+        "allocated_blocks": st["allocated_blocks"],
+        "used_slots": st["used_slots"],
+        "waste_fraction": round(st["waste_fraction"], 5),
+        "contiguous_waste_fraction": round(1 - st["logical_tokens"] / (S * cfg.max_len), 5),
+        "max_sequences_paged": cap,
+        "max_sequences_contiguous": lay.num_blocks * BS // cfg.max_len,
+        "append_ns_per_token": round(t_bulk / max(tokens, 1) * 1e9, 2),
+        "decode_append_us": round(t_step / S * 1e6, 3),
+    }
+
+
 def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -318,6 +377,7 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
         "ops": ops,
+        "allocator": allocator_report(cfg, lay),
     }
     if cfg.prefix_tokens:
         line["unique_bytes_per_launch"] = roof_bytes
