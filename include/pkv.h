@@ -213,6 +213,8 @@ typedef struct {
   int64_t logical_tokens;   /* sum of live sequence lengths                  */
   int64_t copies;           /* copy-on-write pairs handed out so far         */
   int64_t preemptions;      /* sequences released by pkv_bm_preempt so far   */
+  int64_t cached_blocks;    /* full blocks findable by the prefix cache      */
+  int64_t reused_blocks;    /* blocks pkv_bm_add_cached has reused so far    */
 } pkv_bm_stats;
 
 /* Create a manager for num_blocks blocks of block_size slots.  free_order
@@ -240,6 +242,30 @@ pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
 pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t n,
                          int64_t* slots, int64_t* copies, int32_t copies_cap,
                          int32_t* n_copies);
+
+/* Prefix cache.  Requests with identical prefixes can reuse the same
+ * physical blocks, but a paged layout does not find them by itself ("What
+ * does PagedAttention change in LLM KV allocation?", "Sharing requires more
+ * than allocation").  Here a full block is findable under the whole token
+ * prefix it completes while some sequence holds it; lookups use a 64-bit
+ * hash chain over the token ids and confirm every hit against the block's
+ * stored token ids and its predecessor's hash.
+ *
+ * pkv_bm_add_cached starts `seq` for a request of n token ids, reusing the
+ * longest run of findable full blocks from its start (reference counts + 1);
+ * *reused_tokens receives their token count (a multiple of block_size).
+ * The rest of the request is for the caller to store with
+ * pkv_bm_append_tokens, which works like pkv_bm_append and registers the
+ * blocks that become full.  A sequence that gets pkv_bm_append (no token ids)
+ * stops registering blocks.  The first block registered under a prefix keeps
+ * the entry; it is dropped when the block returns to the pool. */
+pkv_status pkv_bm_add_cached(pkv_block_manager* bm, int64_t seq,
+                             const int32_t* tokens, int32_t n,
+                             int32_t* reused_tokens);
+pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, int64_t seq,
+                                const int32_t* tokens, int32_t n,
+                                int64_t* slots, int64_t* copies,
+                                int32_t copies_cap, int32_t* n_copies);
 
 /* Blocks pkv_bm_append(seq, n) would take from the pool (new blocks plus a
  * copy-on-write copy if the last block is shared and not full). */

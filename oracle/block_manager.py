@@ -23,6 +23,14 @@ What it follows:
 * The only waste of a sequence is the unused tail of its last block, less than
   one block ("How PagedAttention works", closing paragraph, and the table
   "Contiguous allocation vs PagedAttention").
+* Prefix caching: requests with identical prefixes can reuse the same
+  physical blocks, but the paged layout does not provide the lookup by itself
+  ("What does PagedAttention change in LLM KV allocation?", "Sharing requires
+  more than allocation").  Reading: a full block is findable under the whole
+  token prefix it completes (positions 0 .. end of the block), while some
+  sequence holds it; a new request reuses the longest run of such blocks from
+  its start.  Blocks filled later through ``append_tokens`` become findable;
+  the first block registered under a prefix keeps the entry.
 """
 
 from collections import deque
@@ -62,6 +70,10 @@ class BlockManager:
         self.fill = [0] * num_blocks
         self.tables = {}
         self.lengths = {}
+        self.tokens = {}          # seq -> token ids, or None when not tracked
+        self.cache = {}           # full token prefix (tuple) -> physical block
+        self.block_key = {}       # physical block -> its prefix key
+        self.reused_blocks = 0
 
     # -- pool -------------------------------------------------------------
     def _take(self):
@@ -77,6 +89,9 @@ class BlockManager:
         if self.refcount[b] == 0:
             self.fill[b] = 0
             self.free.append(b)
+            key = self.block_key.pop(b, None)
+            if key is not None:
+                del self.cache[key]
 
     # -- sequences ----------------------------------------------------------
     def add(self, seq):
@@ -84,8 +99,48 @@ class BlockManager:
             raise KeyError(f"sequence {seq!r} exists")
         self.tables[seq] = []
         self.lengths[seq] = 0
+        self.tokens[seq] = None
 
-    def append(self, seq, n=1):
+    def add_cached(self, seq, tokens):
+        """Start ``seq`` for a request with these token ids, reusing the
+        longest run of findable full blocks from its start.  Returns the number
+        of reused tokens (a multiple of the block size); the rest of the
+        request is for the caller to append."""
+        self.add(seq)
+        BS = self.block_size
+        tokens = [int(t) for t in tokens]
+        n = 0
+        while n + BS <= len(tokens):
+            b = self.cache.get(tuple(tokens[: n + BS]))
+            if b is None:
+                break
+            self.refcount[b] += 1
+            self.tables[seq].append(b)
+            n += BS
+        self.reused_blocks += n // BS
+        self.lengths[seq] = n
+        self.tokens[seq] = tokens[:n]
+        return n
+
+    def append_tokens(self, seq, tokens):
+        """``append`` for a request that carries token ids: blocks that
+        become full are registered under their prefix."""
+        if self.tokens[seq] is None:
+            raise ValueError("sequence does not carry token ids")
+        tokens = [int(t) for t in tokens]
+        start = self.lengths[seq]
+        slots, copies = self.append(seq, len(tokens), keep_tokens=True)
+        self.tokens[seq] += tokens
+        BS = self.block_size
+        for j in range(start // BS, self.lengths[seq] // BS):
+            key = tuple(self.tokens[seq][: (j + 1) * BS])
+            b = self.tables[seq][j]
+            if key not in self.cache and b not in self.block_key:
+                self.cache[key] = b
+                self.block_key[b] = key
+        return slots, copies
+
+    def append(self, seq, n=1, keep_tokens=False):
         """Store ``n`` new tokens of ``seq``.
 
         Returns ``(slots, copies)``: the slot of each new token
@@ -94,6 +149,8 @@ class BlockManager:
         """
         BS = self.block_size
         table = self.tables[seq]
+        if not keep_tokens:
+            self.tokens[seq] = None         # token ids no longer known
         slots, copies = [], []
         for _ in range(n):
             t = self.lengths[seq]
@@ -120,6 +177,8 @@ class BlockManager:
         self.add(child)
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
+        toks = self.tokens[parent]
+        self.tokens[child] = None if toks is None else list(toks)
         for b in self.tables[child]:
             self.refcount[b] += 1
 
@@ -128,6 +187,7 @@ class BlockManager:
         for b in self.tables.pop(seq):
             self._drop(b)
         del self.lengths[seq]
+        del self.tokens[seq]
 
     # -- views --------------------------------------------------------------
     def table_array(self, seqs, width):
@@ -153,4 +213,6 @@ class BlockManager:
             "waste_fraction": (slots - used) / slots if slots else 0.0,
             "free_blocks": len(self.free),
             "sequences": len(self.tables),
+            "cached_blocks": len(self.cache),
+            "reused_blocks": self.reused_blocks,
         }

@@ -30,7 +30,7 @@ class BmStats(ctypes.Structure):
     """Mirror of ``pkv_bm_stats``."""
     _fields_ = [(name, ctypes.c_int64) for name in (
         "allocated_blocks", "allocated_slots", "used_slots", "free_blocks", "sequences",
-        "logical_tokens", "copies", "preemptions")]
+        "logical_tokens", "copies", "preemptions", "cached_blocks", "reused_blocks")]
 
 
 class PkvError(RuntimeError):
@@ -60,6 +60,8 @@ SIGNATURES = {
     "pkv_bm_fork": (_i32, [_vp, _i64, _i64]),
     "pkv_bm_append": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _p(_i32)]),
     "pkv_bm_blocks_needed": (_i32, [_vp, _i64, _i32, _p(_i32)]),
+    "pkv_bm_add_cached": (_i32, [_vp, _i64, _vp, _i32, _p(_i32)]),
+    "pkv_bm_append_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp, _i32, _p(_i32)]),
     "pkv_bm_free": (_i32, [_vp, _i64]),
     "pkv_bm_preempt": (_i32, [_vp, _i64]),
     "pkv_bm_length": (_i32, [_vp, _i64, _p(_i32)]),

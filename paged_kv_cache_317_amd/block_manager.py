@@ -58,6 +58,27 @@ class BlockManager:
                                   copies.ctypes.data, 1, ctypes.byref(ncop)))
         return slots[:n].tolist(), [tuple(r) for r in copies[:ncop.value].tolist()]
 
+    def add_cached(self, seq, tokens):
+        """Start ``seq`` for a request with these token ids, reusing cached
+        full blocks from its start; returns the number of reused tokens."""
+        arr = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = ctypes.c_int32()
+        check(lib().pkv_bm_add_cached(self._h, int(seq), arr.ctypes.data if arr.size else None,
+                                      len(arr), ctypes.byref(out)))
+        return out.value
+
+    def append_tokens(self, seq, tokens):
+        """``append`` with token ids; full blocks become findable."""
+        arr = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = len(arr)
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        copies = np.empty((1, 2), dtype=np.int64)
+        ncop = ctypes.c_int32()
+        check(lib().pkv_bm_append_tokens(self._h, int(seq), arr.ctypes.data if n else None, n,
+                                         slots.ctypes.data, copies.ctypes.data, 1,
+                                         ctypes.byref(ncop)))
+        return slots[:n].tolist(), [tuple(r) for r in copies[:ncop.value].tolist()]
+
     def blocks_needed(self, seq, n):
         out = ctypes.c_int32()
         check(lib().pkv_bm_blocks_needed(self._h, int(seq), int(n), ctypes.byref(out)))

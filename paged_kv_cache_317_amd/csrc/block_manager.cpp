@@ -14,10 +14,31 @@
 
 #include "status.hpp"
 
+namespace {
+
+// 64-bit mixing (the splitmix64 finaliser) and the hash of one full block:
+// its predecessor's hash followed by its token ids.
+inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+inline uint64_t block_hash(uint64_t parent, const int32_t* t, int32_t n) {
+  uint64_t h = mix64(parent ^ 0x9E3779B97F4A7C15ull);
+  for (int32_t i = 0; i < n; ++i) h = mix64(h + (uint32_t)t[i] + 0x9E3779B97F4A7C15ull);
+  return h;
+}
+constexpr uint64_t kRootHash = 0x243F6A8885A308D3ull;   // predecessor of block 0
+
+}  // namespace
+
 struct pkv_block_manager {
   struct Seq {
     std::vector<int32_t> table;   // logical block -> physical block
     int32_t len = 0;
+    bool tracked = false;         // token ids known (prefix-cache registration)
+    std::vector<int32_t> tokens;  // token ids, when tracked
+    std::vector<uint64_t> hashes; // hash chain of the full blocks, when tracked
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
@@ -27,6 +48,54 @@ struct pkv_block_manager {
   std::unordered_map<int64_t, Seq> seqs;
   int64_t copies = 0;
   int64_t preemptions = 0;
+  // Prefix cache: hash -> block, and per registered block its hash, its
+  // predecessor's hash and its token ids (to confirm hits).
+  std::unordered_map<uint64_t, int32_t> cache;
+  std::vector<char> registered;
+  std::vector<uint64_t> reg_hash, reg_parent;
+  std::vector<int32_t> reg_tokens;  // num_blocks x block_size, filled on registration
+  int64_t reused = 0;
+
+  void unregister(int32_t b) {
+    if (!registered.empty() && registered[b]) {
+      cache.erase(reg_hash[b]);
+      registered[b] = 0;
+    }
+  }
+  // Extend a tracked sequence's hash chain over its newly full blocks and
+  // register each one that no entry covers yet.
+  void register_full(Seq& q) {
+    if (registered.empty()) {
+      registered.assign(num_blocks, 0);
+      reg_hash.assign(num_blocks, 0);
+      reg_parent.assign(num_blocks, 0);
+      reg_tokens.assign((size_t)num_blocks * block_size, 0);
+    }
+    const int32_t full = q.len / block_size;
+    for (int32_t j = (int32_t)q.hashes.size(); j < full; ++j) {
+      const int32_t* t = q.tokens.data() + (int64_t)j * block_size;
+      const uint64_t parent = j > 0 ? q.hashes[j - 1] : kRootHash;
+      const uint64_t h = block_hash(parent, t, block_size);
+      q.hashes.push_back(h);
+      const int32_t b = q.table[j];
+      if (registered[b] || cache.count(h)) continue;
+      cache.emplace(h, b);
+      registered[b] = 1;
+      reg_hash[b] = h;
+      reg_parent[b] = parent;
+      std::copy(t, t + block_size, reg_tokens.begin() + (size_t)b * block_size);
+    }
+  }
+  // A registered block holding exactly these tokens after `parent`, or -1.
+  int32_t lookup(uint64_t parent, const int32_t* t) const {
+    const uint64_t h = block_hash(parent, t, block_size);
+    auto it = cache.find(h);
+    if (it == cache.end()) return -1;
+    const int32_t b = it->second;
+    if (reg_parent[b] != parent) return -1;
+    if (!std::equal(t, t + block_size, reg_tokens.begin() + (size_t)b * block_size)) return -1;
+    return b;
+  }
 
   int32_t take() {
     const int32_t b = free_list.front();
@@ -38,6 +107,7 @@ struct pkv_block_manager {
   void drop(int32_t b) {
     if (--refcount[b] == 0) {
       fill[b] = 0;
+      unregister(b);
       free_list.push_back(b);
     }
   }
@@ -128,14 +198,40 @@ PKV_EXPORT pkv_status pkv_bm_blocks_needed(const pkv_block_manager* bm, int64_t 
   return ok();
 }
 
+namespace {
+
+pkv_status append_impl(pkv_block_manager* bm, int64_t seq, bool with_tokens,
+                       const int32_t* tokens, int32_t n, int64_t* slots, int64_t* copies,
+                       int32_t copies_cap, int32_t* n_copies);
+
+}  // namespace
+
 PKV_EXPORT pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t n, int64_t* slots,
                                     int64_t* copies, int32_t copies_cap, int32_t* n_copies) {
+  return append_impl(bm, seq, false, nullptr, n, slots, copies, copies_cap, n_copies);
+}
+
+PKV_EXPORT pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, int64_t seq,
+                                           const int32_t* tokens, int32_t n, int64_t* slots,
+                                           int64_t* copies, int32_t copies_cap,
+                                           int32_t* n_copies) {
+  if (n > 0 && !tokens) return fail(PKV_ERR_NULL, "tokens is NULL");
+  return append_impl(bm, seq, true, tokens, n, slots, copies, copies_cap, n_copies);
+}
+
+namespace {
+
+pkv_status append_impl(pkv_block_manager* bm, int64_t seq, bool with_tokens,
+                       const int32_t* tokens, int32_t n, int64_t* slots, int64_t* copies,
+                       int32_t copies_cap, int32_t* n_copies) {
   pkv_status st = find(bm, seq);
   if (st != PKV_OK) return st;
   if (n < 0) return fail(PKV_ERR_SHAPE, "n must be >= 0");
   if ((n > 0 && !slots) || !n_copies) return fail(PKV_ERR_NULL, "slots and n_copies must be non-NULL");
   pkv_block_manager::Seq& q = bm->seqs.at(seq);
   if ((int64_t)q.len + n > INT32_MAX) return fail(PKV_ERR_SHAPE, "sequence length overflows int32");
+  if (with_tokens && !q.tracked)
+    return fail(PKV_ERR_SHAPE, "sequence %lld does not carry token ids", (long long)seq);
   const int64_t need = bm->needed(q, n);
   const bool cow = n > 0 && q.len % bm->block_size != 0 && bm->refcount[q.table.back()] > 1;
   if (cow && (copies_cap < 1 || !copies))
@@ -170,6 +266,47 @@ PKV_EXPORT pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq, int32_t 
     bm->fill[b] = std::max(bm->fill[b], off + 1);
     q.len = t + 1;
   }
+  if (with_tokens) {
+    q.tokens.insert(q.tokens.end(), tokens, tokens + n);
+    bm->register_full(q);
+  } else if (n > 0) {
+    q.tracked = false;
+    q.tokens.clear();
+    q.hashes.clear();
+  }
+  return ok();
+}
+
+}  // namespace
+
+PKV_EXPORT pkv_status pkv_bm_add_cached(pkv_block_manager* bm, int64_t seq, const int32_t* tokens,
+                                        int32_t n, int32_t* reused_tokens) {
+  if (!bm) return fail(PKV_ERR_NULL, "block manager is NULL");
+  if (n < 0) return fail(PKV_ERR_SHAPE, "n must be >= 0");
+  if ((n > 0 && !tokens) || !reused_tokens)
+    return fail(PKV_ERR_NULL, "tokens and reused_tokens must be non-NULL");
+  if (bm->seqs.count(seq)) return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)seq);
+  pkv_block_manager::Seq q;
+  q.tracked = true;
+  const int32_t BS = bm->block_size;
+  uint64_t parent = kRootHash;
+  int32_t done = 0;
+  while (!bm->cache.empty() && done + BS <= n) {
+    const int32_t b = bm->lookup(parent, tokens + done);
+    if (b < 0) break;
+    parent = bm->reg_hash[b];
+    q.table.push_back(b);
+    done += BS;
+  }
+  for (int32_t b : q.table) {
+    ++bm->refcount[b];
+    q.hashes.push_back(bm->reg_hash[b]);
+  }
+  bm->reused += (int64_t)q.table.size();
+  q.len = done;
+  q.tokens.assign(tokens, tokens + done);
+  bm->seqs.emplace(seq, std::move(q));
+  *reused_tokens = done;
   return ok();
 }
 
@@ -232,6 +369,8 @@ PKV_EXPORT pkv_status pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats
   for (const auto& kv : bm->seqs) s.logical_tokens += kv.second.len;
   s.copies = bm->copies;
   s.preemptions = bm->preemptions;
+  s.cached_blocks = (int64_t)bm->cache.size();
+  s.reused_blocks = bm->reused;
   *out = s;
   return ok();
 }

@@ -214,3 +214,85 @@ def test_capacity_on_a_serving_like_mix():
     assert contig == 20_000 * 16 // 2048
     held = (-(-lens // 16) * 16)[:paged].mean()
     assert abs(paged / contig - 2048 / held) < 0.05
+
+
+# --- prefix cache --------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefix_cache_streams_match_the_oracle(seed):
+    rng = np.random.default_rng(2000 + seed)
+    BS = int(rng.choice([2, 4, 16]))
+    NB = int(rng.integers(60, 200))
+    order = rng.permutation(NB)
+    nat, orc = BlockManager(NB, BS, free_order=order), OracleBM(NB, BS, free_order=order)
+    systems = [rng.integers(0, 50, int(rng.integers(0, 5 * BS))).tolist() for _ in range(3)]
+    live, tracked, next_id = set(), set(), 0
+    for step in range(250):
+        op = rng.choice(["new", "new", "decode", "decode", "fork", "free", "plain"])
+        if op == "new" or not live:
+            prompt = systems[int(rng.integers(0, 3))] + rng.integers(
+                0, 50, int(rng.integers(0, 3 * BS))).tolist()
+            r1 = nat.add_cached(next_id, prompt)
+            r2 = orc.add_cached(next_id, prompt)
+            assert r1 == r2
+            live.add(next_id)
+            tracked.add(next_id)
+            rest = prompt[r1:]
+            if nat.blocks_needed(next_id, len(rest)) <= len(orc.free):
+                assert nat.append_tokens(next_id, rest) == orc.append_tokens(next_id, rest)
+            next_id += 1
+        elif op == "decode":
+            s = int(rng.choice(sorted(live)))
+            toks = rng.integers(0, 50, int(rng.integers(1, BS + 2))).tolist()
+            if nat.blocks_needed(s, len(toks)) > len(orc.free):
+                continue
+            if s in tracked:
+                assert nat.append_tokens(s, toks) == orc.append_tokens(s, toks)
+            else:
+                assert nat.append(s, len(toks)) == orc.append(s, len(toks))
+        elif op == "plain":
+            s = int(rng.choice(sorted(live)))
+            if nat.blocks_needed(s, 1) > len(orc.free):
+                continue
+            assert nat.append(s, 1) == orc.append(s, 1)
+            tracked.discard(s)
+        elif op == "fork":
+            p = int(rng.choice(sorted(live)))
+            nat.fork(p, next_id)
+            orc.fork(p, next_id)
+            live.add(next_id)
+            if p in tracked:
+                tracked.add(next_id)
+            next_id += 1
+        else:
+            s = int(rng.choice(sorted(live)))
+            nat.free_sequence(s)
+            orc.free_sequence(s)
+            live.discard(s)
+            tracked.discard(s)
+        _same_state(nat, orc, live, NB)
+        a, b = nat.stats(), orc.stats()
+        assert a["cached_blocks"] == b["cached_blocks"]
+        assert a["reused_blocks"] == b["reused_blocks"]
+
+
+def test_native_prefix_cache_rebuilds_the_shared_prefix_batch():
+    rng = np.random.default_rng(4)
+    prefix = rng.integers(0, 32000, 1024).tolist()
+    bm = BlockManager(4000, 16)
+    for s in range(128):
+        suffix = rng.integers(0, 32000, int(rng.integers(1, 513))).tolist()
+        reused = bm.add_cached(s, prefix + suffix)
+        assert reused == (0 if s == 0 else 1024)
+        bm.append_tokens(s, (prefix + suffix)[reused:])
+    t = bm.table_array(range(128), 96)
+    assert np.all(t[:, :64] == t[0, :64])
+    st = bm.stats()
+    assert st["reused_blocks"] == 127 * 64
+    with pytest.raises(PkvError):
+        bm.add(0)
+    bm2 = BlockManager(8, 4)
+    bm2.add(0)
+    with pytest.raises(PkvError) as e:
+        bm2.append_tokens(0, [1, 2])              # created without token ids
+    assert e.value.status_name == "PKV_ERR_SHAPE"

@@ -156,3 +156,61 @@ def test_cow_scenario_matches_block_manager(prefix):
     assert np.array_equal(np.array(pairs), sc["pairs"])
     assert np.array_equal(np.array(slots), sc["write_slots"])
     assert np.array_equal(bm.table_array(list(range(S)), cfg.table_width), sc["table_after"])
+
+
+# --- prefix cache --------------------------------------------------------------------
+
+def test_identical_prompt_reuses_its_full_blocks():
+    bm = BlockManager(32, 4)
+    prompt = list(range(100, 111))                 # 11 tokens: 2 full blocks + 3
+    assert bm.add_cached("a", prompt) == 0         # nothing cached yet
+    bm.append_tokens("a", prompt)
+    assert bm.add_cached("b", prompt) == 8         # the two full blocks
+    assert bm.tables["b"] == bm.tables["a"][:2]
+    assert all(bm.refcount[b] == 2 for b in bm.tables["a"][:2])
+    assert bm.refcount[bm.tables["a"][2]] == 1     # partial block not shared
+
+
+def test_reuse_stops_at_the_first_differing_block():
+    bm = BlockManager(32, 4)
+    base = list(range(20))
+    bm.add_cached(0, [])
+    bm.append_tokens(0, base)
+    other = base[:9] + [999] + base[10:]           # differs inside block 2
+    assert bm.add_cached(1, other) == 8
+    assert bm.add_cached(2, [7] + base[1:]) == 0   # differs in block 0
+
+
+def test_nothing_is_found_after_the_holder_leaves():
+    bm = BlockManager(16, 4)
+    bm.add_cached(0, [])
+    bm.append_tokens(0, range(8))
+    bm.free_sequence(0)
+    assert bm.add_cached(1, range(8)) == 0
+    assert bm.stats()["cached_blocks"] == 0
+
+
+def test_plain_append_stops_registration():
+    bm = BlockManager(16, 4)
+    bm.add_cached(0, [])
+    bm.append(0, 8)                                # token ids unknown
+    with pytest.raises(ValueError):
+        bm.append_tokens(0, [1])
+    assert bm.stats()["cached_blocks"] == 0
+
+
+def test_shared_prefix_batch_from_token_ids():
+    """128 requests with one 1024-token prefix share its 64 blocks, as in the
+    shared-prefix workload."""
+    rng = np.random.default_rng(4)
+    prefix = rng.integers(0, 32000, 1024).tolist()
+    bm = BlockManager(4000, 16)
+    for s in range(128):
+        suffix = rng.integers(0, 32000, int(rng.integers(1, 513))).tolist()
+        reused = bm.add_cached(s, prefix + suffix)
+        assert reused == (0 if s == 0 else 1024)
+        bm.append_tokens(s, (prefix + suffix)[reused:])
+    tables = [bm.tables[s][:64] for s in range(128)]
+    assert all(t == tables[0] for t in tables)
+    assert all(bm.refcount[b] == 128 for b in tables[0])
+    assert bm.stats()["reused_blocks"] == 127 * 64
