@@ -75,7 +75,7 @@ def copy_probe(gib, steps, warmup):
 PROFILE = os.path.join(ROOT, "profiles", "paged_attn_decode_c3_gqa4k_bf16.md")
 DECODE_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_decode.hip",
                   "paged_kv_cache_317_amd/csrc/device_common.hpp",
-                  "paged_kv_cache_317_amd/csrc/kernels.hpp"]
+                  "paged_kv_cache_317_amd/csrc/decode.hpp"]
 
 
 def profiled_traffic(workload):
@@ -159,7 +159,7 @@ def time_cache_ops(pkv, w, cfg, dev, per_graph=100, replays=5):
     lay = w.layout
     res = {}
 
-    def timed(fn):
+    def timed(fn, per_graph=per_graph):
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -190,6 +190,24 @@ def time_cache_ops(pkv, w, cfg, dev, per_graph=100, replays=5):
         nbytes = npairs * row * cfg.block_size * 2 * 2
         res["paged_block_copy"] = {"pairs": int(npairs), "us": round(ms * 1e3, 3),
                                    "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    # Swapping: scattered device blocks to a pinned host pool and back.
+    nswap = min(1024, lay.num_blocks)
+    shape = (nswap,) + tuple(w.k_cache.shape[1:])
+    hk = torch.empty(shape, dtype=w.k_cache.dtype).pin_memory()
+    hv = torch.empty(shape, dtype=w.v_cache.dtype).pin_memory()
+    rng = np.random.default_rng(3)
+    dev_ids = rng.choice(lay.num_blocks, size=nswap, replace=False)
+    host_ids = np.arange(nswap)
+    out_pairs = torch.from_numpy(np.stack([dev_ids, host_ids], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([host_ids, dev_ids], 1).astype(np.int64)).to(dev)
+    nbytes = nswap * row * cfg.block_size * 2
+    for key, fn in (("paged_block_move_d2h",
+                     lambda: pkv.paged_block_move(out_pairs, w.k_cache, w.v_cache, hk, hv)),
+                    ("paged_block_move_h2d",
+                     lambda: pkv.paged_block_move(in_pairs, hk, hv, w.k_cache, w.v_cache))):
+        ms = timed(fn, per_graph=5)
+        res[key] = {"blocks": int(nswap), "us": round(ms * 1e3, 3),
+                    "GBps_host_link": round(nbytes / (ms * 1e-3) / 1e9, 1)}
     return res
 
 

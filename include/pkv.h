@@ -215,6 +215,9 @@ typedef struct {
   int64_t preemptions;      /* sequences released by pkv_bm_preempt so far   */
   int64_t cached_blocks;    /* full blocks findable by the prefix cache      */
   int64_t reused_blocks;    /* blocks pkv_bm_add_cached has reused so far    */
+  int64_t host_blocks_used; /* swap space holding swapped-out blocks         */
+  int64_t swapped_sequences;
+  int64_t swap_outs;        /* pkv_bm_swap_out calls so far                  */
 } pkv_bm_stats;
 
 /* Create a manager for num_blocks blocks of block_size slots.  free_order
@@ -272,13 +275,31 @@ pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, int64_t seq,
 pkv_status pkv_bm_blocks_needed(const pkv_block_manager* bm, int64_t seq,
                                 int32_t n, int32_t* blocks);
 
-/* Release a finished sequence; blocks nobody references return to the pool. */
+/* Release a finished sequence; blocks nobody references return to the pool
+ * (for a swapped-out sequence, its host blocks return to the swap space). */
 pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq);
 
 /* Release a sequence the scheduler preempts (its cache is dropped, to be
  * recomputed or restored later; "PagedAttention Explained", "Preemption and
  * scheduling"); counted in pkv_bm_stats.preemptions. */
 pkv_status pkv_bm_preempt(pkv_block_manager* bm, int64_t seq);
+
+/* Preemption by swapping ("PagedAttention Explained", "Preemption and
+ * scheduling").  pkv_bm_set_swap_space gives the manager host_blocks blocks
+ * of host swap space (once).  pkv_bm_swap_out moves `seq` out: every block
+ * of its table, in order, goes to its own free host block, the (device,
+ * host) pairs are written to pairs (host, cap x 2) for pkv_paged_block_move
+ * and *n receives their number; the sequence's device references are
+ * dropped (blocks other sequences share stay for them).  pkv_bm_swap_in
+ * brings it back into fresh device blocks and writes the (host, device)
+ * pairs.  A swapped sequence cannot grow or be forked; sharing and prefix
+ * registration do not survive a swap.  Both fail with PKV_ERR_NO_BLOCKS,
+ * changing nothing, when the target pool is short. */
+pkv_status pkv_bm_set_swap_space(pkv_block_manager* bm, int32_t host_blocks);
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq, int64_t* pairs,
+                           int32_t cap, int32_t* n);
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq, int64_t* pairs,
+                          int32_t cap, int32_t* n);
 
 /* Length (tokens) of a sequence. */
 pkv_status pkv_bm_length(const pkv_block_manager* bm, int64_t seq, int32_t* len);
@@ -300,6 +321,26 @@ pkv_status pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats* out);
 pkv_status pkv_capacity(int64_t num_blocks, int32_t block_size,
                         const int32_t* lens, int32_t n, int32_t reserve_len,
                         int32_t* paged, int32_t* contiguous);
+
+/*
+ * Block move between two pools of the same block shape and dtype (num_blocks
+ * may differ): for each pair i, block pairs[2i+1] of (dst_k, dst_v) becomes
+ * a bit copy of block pairs[2i] of (src_k, src_v).  Either pool may live in
+ * pinned host memory (hipHostMalloc, or a torch tensor with pin_memory):
+ * this moves a preempted sequence's blocks to host memory and back
+ * ("PagedAttention Explained", "Preemption and scheduling"; the pairs come
+ * from pkv_bm_swap_out / pkv_bm_swap_in).  `pairs` may be device or pinned
+ * host memory.  Each pointer is checked with the HIP runtime first: pinned
+ * host memory is reached through its device mapping, and pageable host
+ * memory is refused with PKV_ERR_UNSUPPORTED (no launch).  Pairs naming a
+ * block outside its pool are skipped.  Within one call the destination ids
+ * must be distinct.
+ */
+pkv_status pkv_paged_block_move(const int64_t* pairs, int32_t num_pairs,
+                                const void* src_k, const void* src_v,
+                                const pkv_cache_desc* src, void* dst_k,
+                                void* dst_v, const pkv_cache_desc* dst,
+                                void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);

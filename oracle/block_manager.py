@@ -31,6 +31,13 @@ What it follows:
   sequence holds it; a new request reuses the longest run of such blocks from
   its start.  Blocks filled later through ``append_tokens`` become findable;
   the first block registered under a prefix keeps the entry.
+* Preemption by swapping: a sequence's blocks move to host memory and come
+  back later ("PagedAttention Explained", "Preemption and scheduling").
+  Reading: swap-out copies every block of the sequence, in table order, to
+  its own free host block and drops the sequence's device references (blocks
+  other sequences share stay on the device for them); swap-in takes fresh
+  device blocks in the same order and frees the host blocks.  Sharing is not
+  carried through a swap, and a swapped sequence cannot grow or be forked.
 """
 
 from collections import deque
@@ -74,6 +81,10 @@ class BlockManager:
         self.cache = {}           # full token prefix (tuple) -> physical block
         self.block_key = {}       # physical block -> its prefix key
         self.reused_blocks = 0
+        self.host_free = deque()  # host pool for swapped blocks
+        self.host_blocks = 0
+        self.swapped = {}         # seq -> (host block table, length, tokens)
+        self.swap_outs = 0
 
     # -- pool -------------------------------------------------------------
     def _take(self):
@@ -95,7 +106,7 @@ class BlockManager:
 
     # -- sequences ----------------------------------------------------------
     def add(self, seq):
-        if seq in self.tables:
+        if seq in self.tables or seq in self.swapped:
             raise KeyError(f"sequence {seq!r} exists")
         self.tables[seq] = []
         self.lengths[seq] = 0
@@ -172,6 +183,44 @@ class BlockManager:
             self.lengths[seq] = t + 1
         return slots, copies
 
+    # -- swapping ---------------------------------------------------------------
+    def set_swap_space(self, host_blocks):
+        if self.host_blocks:
+            raise ValueError("swap space is already set")
+        self.host_blocks = host_blocks
+        self.host_free = deque(range(host_blocks))
+
+    def swap_out(self, seq):
+        """Move ``seq`` to host blocks; returns (device, host) block pairs."""
+        table = self.tables[seq]
+        if len(table) > len(self.host_free):
+            raise OutOfBlocks("not enough free host blocks")
+        host = [self.host_free.popleft() for _ in table]
+        pairs = list(zip(table, host))
+        self.swapped[seq] = (host, self.lengths[seq], self.tokens[seq])
+        for b in self.tables.pop(seq):
+            self._drop(b)
+        del self.lengths[seq]
+        del self.tokens[seq]
+        self.swap_outs += 1
+        return pairs
+
+    def swap_in(self, seq):
+        """Bring ``seq`` back to fresh device blocks; returns (host, device) pairs."""
+        host, length, tokens = self.swapped[seq]
+        if len(host) > len(self.free):
+            raise OutOfBlocks("not enough free device blocks")
+        del self.swapped[seq]
+        dev = [self._take() for _ in host]
+        BS = self.block_size
+        for j, b in enumerate(dev):
+            self.fill[b] = min(BS, length - j * BS)
+        self.tables[seq] = dev
+        self.lengths[seq] = length
+        self.tokens[seq] = None            # fresh blocks are not registered
+        self.host_free.extend(host)
+        return list(zip(host, dev))
+
     def fork(self, parent, child):
         """``child`` starts as a copy of ``parent`` that shares all its blocks."""
         self.add(child)
@@ -183,7 +232,11 @@ class BlockManager:
             self.refcount[b] += 1
 
     def free_sequence(self, seq):
-        """Release ``seq``; blocks nobody else references return to the pool."""
+        """Release ``seq``; blocks nobody else references return to the pool
+        (host blocks to the swap space when it is swapped out)."""
+        if seq in self.swapped:
+            self.host_free.extend(self.swapped.pop(seq)[0])
+            return
         for b in self.tables.pop(seq):
             self._drop(b)
         del self.lengths[seq]
@@ -215,4 +268,7 @@ class BlockManager:
             "sequences": len(self.tables),
             "cached_blocks": len(self.cache),
             "reused_blocks": self.reused_blocks,
+            "host_blocks_used": self.host_blocks - len(self.host_free),
+            "swapped_sequences": len(self.swapped),
+            "swap_outs": self.swap_outs,
         }

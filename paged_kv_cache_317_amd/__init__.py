@@ -13,6 +13,7 @@ from .ops import (
     decode_workspace_size,
     paged_attn_decode,
     paged_block_copy,
+    paged_block_move,
     paged_kv_write,
 )
 
@@ -25,5 +26,6 @@ __all__ = [
     "decode_workspace_size",
     "paged_attn_decode",
     "paged_block_copy",
+    "paged_block_move",
     "paged_kv_write",
 ]

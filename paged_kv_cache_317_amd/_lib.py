@@ -30,7 +30,8 @@ class BmStats(ctypes.Structure):
     """Mirror of ``pkv_bm_stats``."""
     _fields_ = [(name, ctypes.c_int64) for name in (
         "allocated_blocks", "allocated_slots", "used_slots", "free_blocks", "sequences",
-        "logical_tokens", "copies", "preemptions", "cached_blocks", "reused_blocks")]
+        "logical_tokens", "copies", "preemptions", "cached_blocks", "reused_blocks",
+        "host_blocks_used", "swapped_sequences", "swap_outs")]
 
 
 class PkvError(RuntimeError):
@@ -54,6 +55,7 @@ SIGNATURES = {
     "pkv_decode_partition_tokens": (_i32, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_decode_workspace_size": (_sz, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_paged_block_copy": (_i32, [_vp, _i32, _vp, _vp, _desc, _vp]),
+    "pkv_paged_block_move": (_i32, [_vp, _i32, _vp, _vp, _desc, _vp, _vp, _desc, _vp]),
     "pkv_bm_create": (_i32, [_i32, _i32, _vp, _p(_vp)]),
     "pkv_bm_destroy": (None, [_vp]),
     "pkv_bm_add": (_i32, [_vp, _i64]),
@@ -63,6 +65,9 @@ SIGNATURES = {
     "pkv_bm_add_cached": (_i32, [_vp, _i64, _vp, _i32, _p(_i32)]),
     "pkv_bm_append_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp, _i32, _p(_i32)]),
     "pkv_bm_free": (_i32, [_vp, _i64]),
+    "pkv_bm_set_swap_space": (_i32, [_vp, _i32]),
+    "pkv_bm_swap_out": (_i32, [_vp, _i64, _vp, _i32, _p(_i32)]),
+    "pkv_bm_swap_in": (_i32, [_vp, _i64, _vp, _i32, _p(_i32)]),
     "pkv_bm_preempt": (_i32, [_vp, _i64]),
     "pkv_bm_length": (_i32, [_vp, _i64, _p(_i32)]),
     "pkv_bm_table": (_i32, [_vp, _vp, _i32, _i32, _vp]),

@@ -90,6 +90,24 @@ class BlockManager:
     def preempt(self, seq):
         check(lib().pkv_bm_preempt(self._h, int(seq)))
 
+    def set_swap_space(self, host_blocks):
+        check(lib().pkv_bm_set_swap_space(self._h, int(host_blocks)))
+
+    def _swap(self, fn, seq):
+        n = ctypes.c_int32()
+        cap = max(self.num_blocks, 1)
+        pairs = np.empty((cap, 2), dtype=np.int64)
+        check(fn(self._h, int(seq), pairs.ctypes.data, cap, ctypes.byref(n)))
+        return [tuple(r) for r in pairs[:n.value].tolist()]
+
+    def swap_out(self, seq):
+        """Move ``seq`` to host swap space; returns (device, host) block pairs."""
+        return self._swap(lib().pkv_bm_swap_out, seq)
+
+    def swap_in(self, seq):
+        """Bring ``seq`` back to fresh device blocks; returns (host, device) pairs."""
+        return self._swap(lib().pkv_bm_swap_in, seq)
+
     def length(self, seq):
         out = ctypes.c_int32()
         check(lib().pkv_bm_length(self._h, int(seq), ctypes.byref(out)))

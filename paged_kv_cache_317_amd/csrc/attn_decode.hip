@@ -49,7 +49,7 @@
 #include <utility>
 
 #include "device_common.hpp"
-#include "kernels.hpp"
+#include "decode.hpp"
 
 namespace pkv {
 namespace {

@@ -1,14 +1,19 @@
-// Block copy: for every (src, dst) pair the whole physical block dst of the K
-// pool and of the V pool becomes a bit copy of block src.  This is the copy
-// step of copy-on-write: a sequence about to write into a block that other
-// sequences still reference gets its own copy first ("PagedAttention
-// Explained", "Sharing blocks between sequences").
+// Whole-block copies between two pools of the same block shape.
+//
+// Copy-on-write: for every (src, dst) pair the block dst of the K pool and of
+// the V pool becomes a bit copy of block src of the same pool -- the copy a
+// sequence takes before writing into a block that others still reference
+// ("PagedAttention Explained", "Sharing blocks between sequences").
+// Swapping: the same copy between the device pool and a pool in pinned host
+// memory, moving a preempted sequence's blocks out and back ("PagedAttention
+// Explained", "Preemption and scheduling").
 //
 // Work split: each workgroup copies one 16 KiB chunk of one block of one pool;
 // every thread issues all its loads before its stores so that four 16-byte
-// loads per thread are in flight.  Pure data movement, HBM bound.
+// loads per thread are in flight.  Pure data movement, bound by HBM (or by
+// the host link when one side is host memory).
 #include "device_common.hpp"
-#include "kernels.hpp"
+#include "cache_ops.hpp"
 
 namespace pkv {
 namespace {
@@ -17,7 +22,7 @@ constexpr int kThreads = 256;
 constexpr int kVecsPerThread = 4;
 constexpr int kChunkVecs = kThreads * kVecsPerThread;   // 16 KiB
 
-__global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a, int chunks) {
+__global__ __launch_bounds__(kThreads) void block_move_kernel(BlockMoveArgs a, int chunks) {
   const int per_pair = 2 * chunks;
   const int pair = blockIdx.x / per_pair;
   const int rem = blockIdx.x - pair * per_pair;
@@ -25,11 +30,10 @@ __global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a, i
   const int chunk = rem - pool * chunks;
   const int64_t src = a.pairs[2 * pair];
   const int64_t dst = a.pairs[2 * pair + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks) return;
   const int64_t block_vecs = a.block_bytes >> 4;
-  uint4* base = reinterpret_cast<uint4*>(pool ? a.v_cache : a.k_cache);
-  const uint4* from = base + src * block_vecs;
-  uint4* to = base + dst * block_vecs;
+  const uint4* from = reinterpret_cast<const uint4*>(pool ? a.src_v : a.src_k) + src * block_vecs;
+  uint4* to = reinterpret_cast<uint4*>(pool ? a.dst_v : a.dst_k) + dst * block_vecs;
   const int64_t first = (int64_t)chunk * kChunkVecs + threadIdx.x;
   uint4 buf[kVecsPerThread];
 #pragma unroll
@@ -46,12 +50,13 @@ __global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a, i
 
 }  // namespace
 
-hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream) {
+hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream) {
   if (a.num_pairs == 0) return hipSuccess;
   const int64_t block_vecs = a.block_bytes >> 4;
   const int chunks = (int)((block_vecs + kChunkVecs - 1) / kChunkVecs);
   const int64_t grid = (int64_t)a.num_pairs * 2 * chunks;
-  hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, chunks);
+  hipLaunchKernelGGL(block_move_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a,
+                     chunks);
   return hipGetLastError();
 }
 

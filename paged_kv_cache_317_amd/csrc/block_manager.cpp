@@ -55,6 +55,15 @@ struct pkv_block_manager {
   std::vector<uint64_t> reg_hash, reg_parent;
   std::vector<int32_t> reg_tokens;  // num_blocks x block_size, filled on registration
   int64_t reused = 0;
+  // Swap space: host block free list and swapped-out sequences.
+  struct Swapped {
+    std::vector<int32_t> host;     // host block of each logical block
+    int32_t len = 0;
+  };
+  int32_t host_blocks = 0;
+  std::deque<int32_t> host_free;
+  std::unordered_map<int64_t, Swapped> swapped;
+  int64_t swap_outs = 0;
 
   void unregister(int32_t b) {
     if (!registered.empty() && registered[b]) {
@@ -173,7 +182,8 @@ PKV_EXPORT void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
 
 PKV_EXPORT pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq) {
   if (!bm) return fail(PKV_ERR_NULL, "block manager is NULL");
-  if (bm->seqs.count(seq)) return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)seq);
+  if (bm->seqs.count(seq) || bm->swapped.count(seq))
+    return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)seq);
   bm->seqs.emplace(seq, pkv_block_manager::Seq{});
   return ok();
 }
@@ -181,7 +191,8 @@ PKV_EXPORT pkv_status pkv_bm_add(pkv_block_manager* bm, int64_t seq) {
 PKV_EXPORT pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
   pkv_status st = find(bm, parent);
   if (st != PKV_OK) return st;
-  if (bm->seqs.count(child)) return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)child);
+  if (bm->seqs.count(child) || bm->swapped.count(child))
+    return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)child);
   pkv_block_manager::Seq copy = bm->seqs.at(parent);
   for (int32_t b : copy.table) ++bm->refcount[b];
   bm->seqs.emplace(child, std::move(copy));
@@ -285,7 +296,8 @@ PKV_EXPORT pkv_status pkv_bm_add_cached(pkv_block_manager* bm, int64_t seq, cons
   if (n < 0) return fail(PKV_ERR_SHAPE, "n must be >= 0");
   if ((n > 0 && !tokens) || !reused_tokens)
     return fail(PKV_ERR_NULL, "tokens and reused_tokens must be non-NULL");
-  if (bm->seqs.count(seq)) return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)seq);
+  if (bm->seqs.count(seq) || bm->swapped.count(seq))
+    return fail(PKV_ERR_KEY, "sequence id %lld exists", (long long)seq);
   pkv_block_manager::Seq q;
   q.tracked = true;
   const int32_t BS = bm->block_size;
@@ -311,6 +323,14 @@ PKV_EXPORT pkv_status pkv_bm_add_cached(pkv_block_manager* bm, int64_t seq, cons
 }
 
 PKV_EXPORT pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq) {
+  if (bm) {
+    auto it = bm->swapped.find(seq);
+    if (it != bm->swapped.end()) {      // finished while swapped out
+      for (int32_t h : it->second.host) bm->host_free.push_back(h);
+      bm->swapped.erase(it);
+      return ok();
+    }
+  }
   pkv_status st = find(bm, seq);
   if (st != PKV_OK) return st;
   bm->release(seq);
@@ -322,6 +342,73 @@ PKV_EXPORT pkv_status pkv_bm_preempt(pkv_block_manager* bm, int64_t seq) {
   if (st != PKV_OK) return st;
   bm->release(seq);
   ++bm->preemptions;
+  return ok();
+}
+
+PKV_EXPORT pkv_status pkv_bm_set_swap_space(pkv_block_manager* bm, int32_t host_blocks) {
+  if (!bm) return fail(PKV_ERR_NULL, "block manager is NULL");
+  if (host_blocks < 1) return fail(PKV_ERR_SHAPE, "host_blocks must be positive");
+  if (bm->host_blocks) return fail(PKV_ERR_SHAPE, "swap space is already set");
+  bm->host_blocks = host_blocks;
+  for (int32_t b = 0; b < host_blocks; ++b) bm->host_free.push_back(b);
+  return ok();
+}
+
+PKV_EXPORT pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq, int64_t* pairs,
+                                      int32_t cap, int32_t* n) {
+  pkv_status st = find(bm, seq);
+  if (st != PKV_OK) return st;
+  if (!n) return fail(PKV_ERR_NULL, "n is NULL");
+  const auto& q = bm->seqs.at(seq);
+  const int64_t need = (int64_t)q.table.size();
+  if (need > 0 && (!pairs || cap < need))
+    return fail(PKV_ERR_SHAPE, "pairs needs room for %lld pairs", (long long)need);
+  if (need > (int64_t)bm->host_free.size())
+    return fail(PKV_ERR_NO_BLOCKS, "swap-out needs %lld host blocks, %zu free", (long long)need,
+                bm->host_free.size());
+  pkv_block_manager::Swapped sw;
+  sw.len = q.len;
+  for (int64_t j = 0; j < need; ++j) {
+    const int32_t h = bm->host_free.front();
+    bm->host_free.pop_front();
+    pairs[2 * j] = q.table[j];
+    pairs[2 * j + 1] = h;
+    sw.host.push_back(h);
+  }
+  *n = (int32_t)need;
+  bm->swapped.emplace(seq, std::move(sw));
+  bm->release(seq);
+  ++bm->swap_outs;
+  return ok();
+}
+
+PKV_EXPORT pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq, int64_t* pairs,
+                                     int32_t cap, int32_t* n) {
+  if (!bm || !n) return fail(PKV_ERR_NULL, "block manager and n must be non-NULL");
+  auto it = bm->swapped.find(seq);
+  if (it == bm->swapped.end())
+    return fail(PKV_ERR_KEY, "sequence id %lld is not swapped out", (long long)seq);
+  const auto& sw = it->second;
+  const int64_t need = (int64_t)sw.host.size();
+  if (need > 0 && (!pairs || cap < need))
+    return fail(PKV_ERR_SHAPE, "pairs needs room for %lld pairs", (long long)need);
+  if (need > (int64_t)bm->free_list.size())
+    return fail(PKV_ERR_NO_BLOCKS, "swap-in needs %lld device blocks, %zu free", (long long)need,
+                bm->free_list.size());
+  pkv_block_manager::Seq q;
+  q.len = sw.len;
+  const int32_t BS = bm->block_size;
+  for (int64_t j = 0; j < need; ++j) {
+    const int32_t b = bm->take();
+    bm->fill[b] = (int32_t)std::min<int64_t>(BS, sw.len - j * BS);
+    q.table.push_back(b);
+    pairs[2 * j] = sw.host[j];
+    pairs[2 * j + 1] = b;
+    bm->host_free.push_back(sw.host[j]);
+  }
+  *n = (int32_t)need;
+  bm->swapped.erase(it);
+  bm->seqs.emplace(seq, std::move(q));
   return ok();
 }
 
@@ -371,6 +458,9 @@ PKV_EXPORT pkv_status pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats
   s.preemptions = bm->preemptions;
   s.cached_blocks = (int64_t)bm->cache.size();
   s.reused_blocks = bm->reused;
+  s.host_blocks_used = bm->host_blocks - (int64_t)bm->host_free.size();
+  s.swapped_sequences = (int64_t)bm->swapped.size();
+  s.swap_outs = bm->swap_outs;
   *out = s;
   return ok();
 }

@@ -1,4 +1,4 @@
-// Internal launchers of the HIP kernels (host side).  The C ABI in
+// Internal launchers of the decode kernels (host side).  The C ABI in
 // pkv_api.cpp validates every argument and then calls these.
 #pragma once
 
@@ -9,26 +9,6 @@ namespace pkv {
 
 // Largest number of table entries one decode partition stages in LDS.
 constexpr int kMaxPartBlocks = 512;
-
-struct KvWriteArgs {
-  const void* k;
-  const void* v;
-  const int64_t* slot_mapping;
-  int64_t num_tokens;
-  void* k_cache;
-  void* v_cache;
-  int64_t num_slots;     // num_blocks * block_size
-  int64_t row_bytes;     // kv_heads * head_dim * element bytes, multiple of 16
-};
-
-struct BlockCopyArgs {
-  const int64_t* pairs;
-  int32_t num_pairs;
-  void* k_cache;
-  void* v_cache;
-  int64_t num_blocks;
-  int64_t block_bytes;   // block_size * kv_heads * head_dim * element bytes
-};
 
 struct DecodeArgs {
   const void* q;
@@ -53,9 +33,6 @@ struct DecodeArgs {
   uint32_t block_bytes;    // block_size slots
   float scale_log2;        // scale * log2(e)
 };
-
-hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
-hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream);
 
 // dtype: 0 f32, 1 bf16.  Returns hipErrorInvalidValue for a combination
 // with no instantiated kernel (the API layer checks first).

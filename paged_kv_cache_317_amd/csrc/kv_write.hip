@@ -10,7 +10,7 @@
 // consecutive pieces of the same row, so each wave reads and writes 1 KiB
 // contiguous spans.  Pure data movement, HBM bound.
 #include "device_common.hpp"
-#include "kernels.hpp"
+#include "cache_ops.hpp"
 
 namespace pkv {
 namespace {

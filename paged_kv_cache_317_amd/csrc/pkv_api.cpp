@@ -10,7 +10,8 @@
 #include <string>
 
 #include "../../include/pkv.h"
-#include "kernels.hpp"
+#include "cache_ops.hpp"
+#include "decode.hpp"
 #include "status.hpp"
 
 namespace pkv {
@@ -258,16 +259,88 @@ PKV_EXPORT pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pai
     return fail(PKV_ERR_NULL, "pairs, k_cache and v_cache must be non-NULL");
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_ALIGN, "k_cache and v_cache must be 16-byte aligned");
-  pkv::BlockCopyArgs a;
+  pkv::BlockMoveArgs a;
   a.pairs = pairs;
   a.num_pairs = num_pairs;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.num_blocks = cache->num_blocks;
+  a.src_k = k_cache;
+  a.src_v = v_cache;
+  a.dst_k = k_cache;
+  a.dst_v = v_cache;
+  a.src_blocks = a.dst_blocks = cache->num_blocks;
   a.block_bytes = (int64_t)cache->block_size * cache->kv_heads * cache->head_dim *
                   elem_bytes(cache->dtype);
   const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
   if ((int64_t)num_pairs * 2 * chunks > INT32_MAX)
     return fail(PKV_ERR_SHAPE, "too many pairs for one launch");
-  return from_hip(pkv::launch_block_copy(a, (hipStream_t)stream), "paged_block_copy launch");
+  return from_hip(pkv::launch_block_move(a, (hipStream_t)stream), "paged_block_copy launch");
+}
+
+namespace {
+
+// The address a kernel uses for `p`: device memory as is, pinned host memory
+// through its device mapping.  Pageable host memory (or anything the runtime
+// does not know) is refused, so a kernel never dereferences it.
+pkv_status device_address(const void* p, const char* name, void** out) {
+  hipPointerAttribute_t attr{};
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_UNSUPPORTED, "%s is neither device memory nor pinned host memory", name);
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = const_cast<void*>(p);
+    return PKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, const_cast<void*>(p), 0);
+    if (e != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return fail(PKV_ERR_UNSUPPORTED, "%s is host memory without a device mapping", name);
+    }
+    *out = d;
+    return PKV_OK;
+  }
+  return fail(PKV_ERR_UNSUPPORTED, "%s is neither device memory nor pinned host memory", name);
+}
+
+}  // namespace
+
+PKV_EXPORT pkv_status pkv_paged_block_move(const int64_t* pairs, int32_t num_pairs,
+                                           const void* src_k, const void* src_v,
+                                           const pkv_cache_desc* src, void* dst_k, void* dst_v,
+                                           const pkv_cache_desc* dst, void* stream) {
+  pkv_status st = check_cache(src);
+  if (st != PKV_OK) return st;
+  st = check_cache(dst);
+  if (st != PKV_OK) return st;
+  if (src->block_size != dst->block_size || src->kv_heads != dst->kv_heads ||
+      src->head_dim != dst->head_dim || src->dtype != dst->dtype)
+    return fail(PKV_ERR_SHAPE, "source and destination pools must have the same block shape and dtype");
+  if (num_pairs < 0) return fail(PKV_ERR_SHAPE, "num_pairs must be >= 0");
+  if (num_pairs == 0) return ok();
+  if (!pairs || !src_k || !src_v || !dst_k || !dst_v)
+    return fail(PKV_ERR_NULL, "pairs and the four pool pointers must be non-NULL");
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return fail(PKV_ERR_ALIGN, "pool pointers must be 16-byte aligned");
+  pkv::BlockMoveArgs a;
+  void* p = nullptr;
+  if ((st = device_address(pairs, "pairs", &p)) != PKV_OK) return st;
+  a.pairs = static_cast<const int64_t*>(p);
+  if ((st = device_address(src_k, "src_k", &p)) != PKV_OK) return st;
+  a.src_k = p;
+  if ((st = device_address(src_v, "src_v", &p)) != PKV_OK) return st;
+  a.src_v = p;
+  if ((st = device_address(dst_k, "dst_k", &p)) != PKV_OK) return st;
+  a.dst_k = p;
+  if ((st = device_address(dst_v, "dst_v", &p)) != PKV_OK) return st;
+  a.dst_v = p;
+  a.num_pairs = num_pairs;
+  a.src_blocks = src->num_blocks;
+  a.dst_blocks = dst->num_blocks;
+  a.block_bytes = (int64_t)src->block_size * src->kv_heads * src->head_dim * elem_bytes(src->dtype);
+  const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
+  if ((int64_t)num_pairs * 2 * chunks > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "too many pairs for one launch");
+  return from_hip(pkv::launch_block_move(a, (hipStream_t)stream), "paged_block_move launch");
 }

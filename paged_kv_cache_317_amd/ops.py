@@ -128,3 +128,32 @@ def paged_block_copy(pairs, k_cache, v_cache):
     with torch.cuda.device(dev):
         check(lib().pkv_paged_block_copy(_ptr(pairs), n, _ptr(k_cache), _ptr(v_cache),
                                          ctypes.byref(desc), _stream(dev)))
+
+
+def paged_block_move(pairs, src_k, src_v, dst_k, dst_v):
+    """Copy blocks ``pairs[i, 0]`` of (src_k, src_v) to ``pairs[i, 1]`` of
+    (dst_k, dst_v); either pool may be a pinned host tensor.  Runs on the
+    current stream of the GPU side."""
+    for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device.type == "cpu" and not t.is_pinned():
+            raise ValueError(f"{name} is host memory that is not pinned")
+    if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape:
+        raise ValueError("K and V pools of one side must have the same shape")
+    if src_k.dtype != dst_k.dtype or src_v.dtype != dst_v.dtype or src_k.dtype != src_v.dtype:
+        raise TypeError("all pools must share one dtype")
+    gpu = [t.device for t in (src_k, dst_k, pairs) if t.device.type == "cuda"]
+    if not gpu:
+        raise ValueError("at least one side must be on a GPU")
+    dev = gpu[0]
+    n = pairs.shape[0] if pairs.dim() == 2 else -1
+    if tuple(pairs.shape) != (n, 2) or pairs.dtype != torch.int64 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous int64 [n, 2] tensor")
+    if pairs.device.type == "cpu" and not pairs.is_pinned():
+        raise ValueError("host pairs must be pinned")
+    sdesc, ddesc = cache_desc(src_k), cache_desc(dst_k)
+    with torch.cuda.device(dev):
+        check(lib().pkv_paged_block_move(_ptr(pairs), n, _ptr(src_k), _ptr(src_v),
+                                         ctypes.byref(sdesc), _ptr(dst_k), _ptr(dst_v),
+                                         ctypes.byref(ddesc), _stream(dev)))

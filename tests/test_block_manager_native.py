@@ -296,3 +296,102 @@ def test_native_prefix_cache_rebuilds_the_shared_prefix_batch():
     with pytest.raises(PkvError) as e:
         bm2.append_tokens(0, [1, 2])              # created without token ids
     assert e.value.status_name == "PKV_ERR_SHAPE"
+
+
+# --- swapping -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_swap_streams_match_the_oracle(seed):
+    """Random add/fork/append/free/swap-out/swap-in streams: same pairs, tables
+    and counters as the oracle, and refusals where it runs short."""
+    rng = np.random.default_rng(3000 + seed)
+    NB, BS, HB = int(rng.integers(30, 100)), int(rng.choice([1, 4, 16])), int(rng.integers(5, 60))
+    order = rng.permutation(NB)
+    nat, orc = BlockManager(NB, BS, free_order=order), OracleBM(NB, BS, free_order=order)
+    nat.set_swap_space(HB)
+    orc.set_swap_space(HB)
+    live, out, next_id = set(), set(), 0
+    for step in range(300):
+        op = rng.choice(["add", "fork", "append", "append", "free", "out", "out", "in"])
+        if op == "add" or not (live or out):
+            nat.add(next_id)
+            orc.add(next_id)
+            live.add(next_id)
+            next_id += 1
+        elif op == "fork" and live:
+            p = int(rng.choice(sorted(live)))
+            nat.fork(p, next_id)
+            orc.fork(p, next_id)
+            live.add(next_id)
+            next_id += 1
+        elif op == "append" and live:
+            s = int(rng.choice(sorted(live)))
+            n = int(rng.integers(0, 3 * BS + 2))
+            if nat.blocks_needed(s, n) > len(orc.free):
+                continue
+            assert nat.append(s, n) == orc.append(s, n)
+        elif op == "free":
+            s = int(rng.choice(sorted(live | out)))
+            nat.free_sequence(s)
+            orc.free_sequence(s)
+            live.discard(s)
+            out.discard(s)
+        elif op == "out" and live:
+            s = int(rng.choice(sorted(live)))
+            if len(orc.tables[s]) > len(orc.host_free):
+                with pytest.raises(PkvError) as e:
+                    nat.swap_out(s)
+                assert e.value.status_name == "PKV_ERR_NO_BLOCKS"
+                continue
+            assert nat.swap_out(s) == orc.swap_out(s)
+            live.discard(s)
+            out.add(s)
+            with pytest.raises(PkvError) as e:
+                nat.append(s, 1)                  # swapped: cannot grow
+            assert e.value.status_name == "PKV_ERR_KEY"
+        elif op == "in" and out:
+            s = int(rng.choice(sorted(out)))
+            if len(orc.swapped[s][0]) > len(orc.free):
+                before = nat.stats()
+                with pytest.raises(PkvError) as e:
+                    nat.swap_in(s)
+                assert e.value.status_name == "PKV_ERR_NO_BLOCKS"
+                assert nat.stats() == before
+                continue
+            assert nat.swap_in(s) == orc.swap_in(s)
+            out.discard(s)
+            live.add(s)
+        _same_state(nat, orc, live, NB)
+        a, b = nat.stats(), orc.stats()
+        for k in ("host_blocks_used", "swapped_sequences", "swap_outs"):
+            assert a[k] == b[k], k
+
+
+def test_swap_round_trip_keeps_length_and_fill():
+    bm = BlockManager(8, 4)
+    bm.set_swap_space(4)
+    bm.add(0)
+    bm.append(0, 10)                                # 3 blocks, last holds 2
+    bm.fork(0, 1)
+    pairs = bm.swap_out(0)
+    assert [h for _, h in pairs] == [0, 1, 2]
+    st = bm.stats()
+    assert st["allocated_blocks"] == 3              # still held by sequence 1
+    assert st["host_blocks_used"] == 3 and st["swapped_sequences"] == 1
+    with pytest.raises(PkvError):
+        bm.fork(0, 2)
+    with pytest.raises(PkvError):
+        bm.add(0)
+    back = bm.swap_in(0)
+    assert [h for h, _ in back] == [0, 1, 2]
+    assert bm.length(0) == 10
+    st = bm.stats()
+    assert st["allocated_blocks"] == 6 and st["used_slots"] == 20
+    assert st["host_blocks_used"] == 0 and st["swap_outs"] == 1
+    _, copies = bm.append(0, 1)                     # own blocks now: no copy
+    assert copies == []
+    with pytest.raises(PkvError) as e:
+        bm.swap_in(0)
+    assert e.value.status_name == "PKV_ERR_KEY"
+    with pytest.raises(PkvError):
+        bm.set_swap_space(8)                        # set once

@@ -214,3 +214,55 @@ def test_shared_prefix_batch_from_token_ids():
     assert all(t == tables[0] for t in tables)
     assert all(bm.refcount[b] == 128 for b in tables[0])
     assert bm.stats()["reused_blocks"] == 127 * 64
+
+
+# --- swapping ------------------------------------------------------------------------
+
+def test_swap_out_and_in_round_trip():
+    bm = BlockManager(8, 4)
+    bm.set_swap_space(6)
+    bm.add(0)
+    bm.append(0, 10)                             # 3 blocks, last holds 2
+    table = list(bm.tables[0])
+    out = bm.swap_out(0)
+    assert [d for d, _ in out] == table and len({h for _, h in out}) == 3
+    st = bm.stats()
+    assert st["allocated_blocks"] == 0 and st["host_blocks_used"] == 3
+    assert st["swapped_sequences"] == 1 and st["swap_outs"] == 1
+    back = bm.swap_in(0)
+    assert [h for h, _ in back] == [h for _, h in out]
+    assert bm.lengths[0] == 10 and len(bm.tables[0]) == 3
+    assert bm.stats()["used_slots"] == 10 and bm.stats()["host_blocks_used"] == 0
+    slots, _ = bm.append(0, 1)                   # grows again in its last block
+    assert slots == [bm.tables[0][2] * 4 + 2]
+
+
+def test_swap_keeps_shared_blocks_for_the_others():
+    bm = BlockManager(8, 4)
+    bm.set_swap_space(8)
+    bm.add(0)
+    bm.append(0, 8)
+    bm.fork(0, 1)
+    bm.swap_out(1)
+    assert all(bm.refcount[b] == 1 for b in bm.tables[0])
+    bm.swap_in(1)
+    assert set(bm.tables[1]).isdisjoint(bm.tables[0])   # no sharing after a swap
+
+
+def test_swap_refusals_and_free_while_swapped():
+    bm = BlockManager(5, 4)
+    bm.set_swap_space(2)
+    bm.add(0)
+    bm.append(0, 12)                             # 3 blocks > 2 host blocks
+    with pytest.raises(OutOfBlocks):
+        bm.swap_out(0)
+    assert bm.lengths[0] == 12 and bm.stats()["host_blocks_used"] == 0
+    bm.add(1)
+    bm.append(1, 5)
+    bm.swap_out(1)
+    bm.append(0, 4)                              # takes one of the two freed blocks
+    with pytest.raises(OutOfBlocks):
+        bm.swap_in(1)                            # needs 2, device has 1
+    bm.free_sequence(1)                          # finished while swapped out
+    st = bm.stats()
+    assert st["host_blocks_used"] == 0 and st["swapped_sequences"] == 0
