@@ -29,6 +29,8 @@ Modules
 ``bf16``           exact widening of bfloat16 bit patterns to float64.
 ``attention``      decode attention over a paged cache (materialise, then
                    attend), the split-K partition states and their merge.
+``extend``         multi-token (prefill / chunked extend) causal attention
+                   over a paged cache.
 ``cache_ops``      slot write and block copy (bitwise).
 ``block_manager``  on-demand allocation, reference counts, copy-on-write,
                    release, and waste accounting.
@@ -47,6 +49,7 @@ from .attention import (
     merge_states,
     split_decode_attention,
 )
+from .extend import extend_attention, extend_flops
 from .cache_ops import kv_write, block_copy
 from .block_manager import BlockManager, OutOfBlocks, blocks_for, tail_waste
 
@@ -57,6 +60,8 @@ __all__ = [
     "partition_states",
     "merge_states",
     "split_decode_attention",
+    "extend_attention",
+    "extend_flops",
     "kv_write",
     "block_copy",
     "BlockManager",

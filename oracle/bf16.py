@@ -13,9 +13,14 @@ def widen(values, dtype):
     """Return ``values`` as float64, exactly.
 
     ``dtype`` names how ``values`` is stored: ``"f32"`` for float32 arrays,
-    ``"bf16"`` for uint16 arrays holding bfloat16 bit patterns.
+    ``"bf16"`` for uint16 arrays holding bfloat16 bit patterns, ``"f64"`` for
+    float64 arrays (returned as they are; used by pins on float64 inputs).
     """
     a = np.asarray(values)
+    if dtype == "f64":
+        if a.dtype != np.float64:
+            raise TypeError(f"f64 data must be float64, got {a.dtype}")
+        return a
     if dtype == "f32":
         if a.dtype != np.float32:
             raise TypeError(f"f32 data must be float32, got {a.dtype}")

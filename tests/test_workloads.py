@@ -88,3 +88,38 @@ def test_cow_layout_pairs_and_tables():
     assert np.all(sc["table_after"][127] == sc["table_before"][127])
     assert np.all(sc["table_after"][:127, 63] == sc["pairs"][:, 1])
     assert np.all(sc["write_slots"] % 16 == 8)
+
+
+# --- prefill / extend batches ------------------------------------------------------
+
+from workloads import EXTEND_CONFIGS, extend_slots, generate_extend_host  # noqa: E402
+
+
+@pytest.mark.parametrize("name", ["x1_extend_tiny_bf16", "x4_extend_g8_bs32_bf16",
+                                  "x5_extend_mha_bf16"])
+def test_extend_batches_are_consistent(name):
+    cfg = EXTEND_CONFIGS[name]
+    w = generate_extend_host(cfg)
+    lay, BS = w.layout, cfg.block_size
+    new = np.diff(w.query_start)
+    assert np.array_equal(lay.seq_lens, w.ctx_lens + new)
+    assert w.q.shape == (w.num_tokens, cfg.q_heads, cfg.head_dim)
+    assert w.new_k.shape == (w.num_tokens, cfg.kv_heads, cfg.head_dim)
+    used = lay.block_table[lay.block_table >= 0]
+    assert np.unique(used).size == used.size and used.max() < lay.num_blocks
+    slots = w.slot_mapping
+    assert np.unique(slots).size == slots.size
+    for s in range(cfg.num_seqs):
+        for j in range(int(new[s])):
+            t = int(w.ctx_lens[s]) + j
+            row = int(w.query_start[s]) + j
+            assert slots[row] == lay.block_table[s, t // BS] * BS + t % BS
+    again = generate_extend_host(cfg)
+    assert np.array_equal(again.q, w.q) and np.array_equal(again.k_cache, w.k_cache)
+
+
+def test_extend_slots_of_a_hand_made_table():
+    table = np.array([[5, 2, -1], [0, 7, 3]], dtype=np.int32)
+    slots = extend_slots(table, np.array([6, 9]), np.array([0, 3, 5]), 4)
+    # sequence 0: positions 3, 4, 5; sequence 1: positions 7, 8
+    assert slots.tolist() == [5 * 4 + 3, 2 * 4 + 0, 2 * 4 + 1, 7 * 4 + 3, 3 * 4 + 0]

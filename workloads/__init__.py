@@ -2,8 +2,9 @@
 
 This package builds inputs only: sequence lengths, pools, block tables,
 queries, cache contents, new-token rows, slot mappings and copy-on-write
-pairs.  It holds none of the attention arithmetic and imports neither the
-oracle nor the HIP binding, so both sides can be fed from it.
+pairs, for decode batches and for prefill / chunked-extend batches.  It
+holds none of the attention arithmetic and imports neither the oracle nor
+the HIP binding, so both sides can be fed from it.
 """
 
 from .configs import CONFIGS, DecodeConfig, get_config, scaled
@@ -16,6 +17,16 @@ from .generate import (
     generate_host,
     generate_device,
     f32_to_bf16_bits,
+)
+from .extend import (
+    EXTEND_CONFIGS,
+    ExtendConfig,
+    ExtendWorkload,
+    extend_layout,
+    extend_slots,
+    generate_extend_device,
+    generate_extend_host,
+    get_extend_config,
 )
 
 __all__ = [
@@ -31,4 +42,12 @@ __all__ = [
     "generate_host",
     "generate_device",
     "f32_to_bf16_bits",
+    "EXTEND_CONFIGS",
+    "ExtendConfig",
+    "ExtendWorkload",
+    "extend_layout",
+    "extend_slots",
+    "generate_extend_device",
+    "generate_extend_host",
+    "get_extend_config",
 ]
