@@ -16,6 +16,11 @@ timed with events recorded on the launch stream around it in every timed step.
 same batch.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+With a prefill/extend workload (``--workload x2_prefill_bf16`` or
+``x3_extend_bf16``) the step is the slot write of every new token followed by
+``paged_attn_extend``, and ``value`` is the causal attention's TFLOP/s
+against the bf16 matrix-core peak.
 """
 
 import argparse
@@ -270,6 +275,150 @@ def allocator_report(cfg, lay):
     }
 
 
+EXTEND_METRIC = "paged prefill/extend attention: causal TFLOP/s, 1 GPU"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
+
+
+def causal_work(lens, query_start, q_heads, head_dim):
+    """(flops, query positions) of a prefill/extend batch: a query at
+    position p takes p + 1 logits and as many weighted value rows per head,
+    2 * head_dim flops each."""
+    import numpy as np
+    qs = np.asarray(query_start, dtype=np.int64)
+    n = np.diff(qs)
+    keys = 0
+    for s in range(n.size):
+        p = int(lens[s]) - int(n[s]) + np.arange(int(n[s]))
+        keys += int(np.clip(p + 1, 0, None).sum())
+    return keys * q_heads * 4 * head_dim, keys
+
+
+def extend_bench(args):
+    """Prefill / chunked-extend step: slot write of every new token, then the
+    causal attention of all new tokens over the paged cache."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_317_amd as pkv
+    from paged_kv_cache_317_amd.build import ensure_built
+    from workloads import EXTEND_CONFIGS, generate_extend_device
+
+    ensure_built()
+    cfg = EXTEND_CONFIGS[args.workload]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"# workload {cfg.name}: generating on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    w = generate_extend_device(cfg, device=dev)
+    lay = w.layout
+    maxq = w.max_query_len
+    out = torch.empty_like(w.q)
+
+    def write():
+        pkv.paged_kv_write(w.new_k, w.new_v, w.slot_mapping, w.k_cache, w.v_cache)
+
+    def attend():
+        pkv.paged_attn_extend(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens,
+                              w.query_start_dev, cfg.scale, maxq, out=out)
+
+    for _ in range(args.warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        write()
+        ev[i][0].record()
+        attend()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = wall * 1e3 / K
+    print(f"# {K} steps: {step_ms:.4f} ms/step, extend {attn_ms:.4f} ms", file=sys.stderr,
+          flush=True)
+    flops, _ = causal_work(lay.seq_lens, w.query_start, cfg.q_heads, cfg.head_dim)
+    T = w.num_tokens
+    row = cfg.kv_heads * cfg.head_dim * cfg.elem_bytes
+    kv_bytes = int(lay.seq_lens.astype(np.int64).sum()) * row * 2
+    io_bytes = 2 * T * cfg.q_heads * cfg.head_dim * cfg.elem_bytes
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+        # A bounded sample: the new tokens (at most 1024) of the shortest sequence.
+        s = int(np.argmin(lay.seq_lens))
+        qs = w.query_start
+        nq = min(int(qs[s + 1] - qs[s]), 1024)
+        q = host_array(w.q)[qs[s]:qs[s] + nq]
+        kc, vc = host_array(w.k_cache), host_array(w.v_cache)
+        L = int(lay.seq_lens[s])
+        n_all = int(qs[s + 1] - qs[s])
+        # the sample's own sequence: its first nq queries at their true positions
+        lens = np.array([L - n_all + nq])
+        sflops, _ = causal_work(lens, np.array([0, nq]), cfg.q_heads, cfg.head_dim)
+        import threadpoolctl
+        with threadpoolctl.threadpool_limits(1):
+            t1 = time.perf_counter()
+            oracle.extend_attention(q, kc, vc, lay.block_table[s:s + 1], lens,
+                                    np.array([0, nq]), cfg.scale, cfg.dtype)
+            dt = time.perf_counter() - t1
+        cpu = {"value": round(sflops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+               "kind": "oracle", "wall_s": round(dt, 3),
+               "sample": f"first {nq} new tokens of sequence {s} (length {L}) of the same "
+                         f"batch, fp64 numpy, BLAS limited to 1 thread"}
+
+    line = {
+        "metric": EXTEND_METRIC,
+        "value": round(achieved, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded, drawn on the device)",
+        "config": {
+            "workload": cfg.name,
+            "num_seqs": cfg.num_seqs,
+            "q_heads": cfg.q_heads,
+            "kv_heads": cfg.kv_heads,
+            "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size,
+            "new_tokens": T,
+            "seq_lens": [int(lay.seq_lens.min()), int(lay.seq_lens.max())],
+            "pool_blocks": lay.num_blocks,
+            "step": "paged_kv_write (every new token) + paged_attn_extend",
+        },
+        "tokens_per_s": round(T / (step_ms * 1e-3), 1),
+        "extend_ms": round(attn_ms, 5),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "paged_attn_extend",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops,
+            "kv_bytes_per_launch": kv_bytes + io_bytes,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -280,6 +429,10 @@ def main(argv=None):
 
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe, args.steps, args.warmup)
+
+    from workloads import EXTEND_CONFIGS
+    if args.workload in EXTEND_CONFIGS:
+        return extend_bench(args)
 
     import numpy as np
     import torch

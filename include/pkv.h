@@ -145,6 +145,44 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Attention of several new tokens per sequence over a paged cache: a prefill
+ * (nothing cached yet), or a chunk of new tokens on top of a cached context.
+ * The new tokens' K/V rows must already be in the cache (pkv_paged_kv_write).
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1; with
+ * n = query_start[s+1] - query_start[s] and L = seq_lens[s] (new tokens
+ * included), query j sits at position p = L - n + j and, for each query head
+ * h with kv head g = h / G,
+ *     out[row,h,:] = sum_{t<=p} softmax_t(scale * q[row,h,:] . K_s[t,g,:]) V_s[t,g,:]
+ * (causal: each new token sees the context and the new tokens up to itself;
+ * "PagedAttention Explained", "How PagedAttention works", step 5, and
+ * "Preemption and scheduling" for the prefill pass that recomputes a
+ * sequence).  A query with p < 0 gets a zero row.  Keys stop at
+ * table_width * block_size and at the first table entry outside the pool.
+ * Arithmetic: bf16 products summed in fp32 for the logits, softmax in fp32,
+ * the weights rounded to bf16 for the weighted sum of V (fp32 accumulation),
+ * the output rounded to nearest even bf16.
+ *   q, out       device, [num_tokens, q_heads, head_dim]
+ *   block_table  device, int32 [num_seqs, table_width]
+ *   seq_lens     device, int32 [num_seqs]
+ *   query_start  device, int32 [num_seqs + 1], non-decreasing, from 0 to
+ *                num_tokens; rows outside [0, num_tokens) are never read or
+ *                written whatever it holds
+ *   max_query_len host-side bound on every n (sizes the grid); query rows
+ *                j >= max_query_len of a sequence are not written
+ * No workspace.  Supported: bf16 caches with head_dim 128, block_size 16 or
+ * 32, G in {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.
+ */
+pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache,
+                                 const void* v_cache,
+                                 const pkv_cache_desc* cache,
+                                 const int32_t* block_table,
+                                 int32_t table_width, const int32_t* seq_lens,
+                                 const int32_t* query_start, int32_t num_seqs,
+                                 int32_t num_tokens, int32_t q_heads,
+                                 int32_t max_query_len, float scale, void* out,
+                                 void* stream);
+
+/*
  * Partition length (tokens) pkv_paged_attn_decode uses for these arguments;
  * the call is split when it is below max_seq_len.  Returns 0 on invalid
  * arguments (see pkv_last_error()).

@@ -12,6 +12,7 @@ from .ops import (
     decode_partition_tokens,
     decode_workspace_size,
     paged_attn_decode,
+    paged_attn_extend,
     paged_block_copy,
     paged_block_move,
     paged_kv_write,
@@ -25,6 +26,7 @@ __all__ = [
     "decode_partition_tokens",
     "decode_workspace_size",
     "paged_attn_decode",
+    "paged_attn_extend",
     "paged_block_copy",
     "paged_block_move",
     "paged_kv_write",

@@ -1,0 +1,39 @@
+// Internal launcher of the multi-token (prefill / extend) attention kernel
+// (host side).  The C ABI in pkv_api.cpp validates every argument first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct ExtendArgs {
+  const void* q;               // [T, q_heads, head_dim]
+  const void* k_cache;
+  const void* v_cache;
+  void* out;                   // [T, q_heads, head_dim]
+  const int32_t* block_table;  // [num_seqs, table_width]
+  const int32_t* seq_lens;     // [num_seqs], new tokens included
+  const int32_t* query_start;  // [num_seqs + 1]
+  int64_t num_blocks;
+  int32_t table_width;
+  int32_t num_seqs;
+  int32_t num_tokens;          // rows of q and out; rows at or past it are never touched
+  int32_t q_heads;
+  int32_t kv_heads;
+  int32_t max_query_len;       // host bound on query_start[s+1] - query_start[s]
+  int32_t q_tiles;             // query tiles per (sequence, kv head)
+  int32_t units;               // num_seqs * kv_heads * q_tiles
+  uint32_t row_bytes;          // one slot: kv_heads * head_dim * element bytes
+  uint32_t block_bytes;        // block_size slots
+  float scale_log2;            // scale * log2(e)
+};
+
+// Query columns (token, head) one workgroup covers; a workgroup holds
+// kExtendCols / G query tokens of one sequence.
+constexpr int kExtendCols = 128;
+
+bool extend_supported(int dtype, int head_dim, int block_size, int group);
+hipError_t launch_extend(const ExtendArgs& a, int block_size, int group, hipStream_t stream);
+
+}  // namespace pkv

@@ -12,6 +12,7 @@
 #include "../../include/pkv.h"
 #include "cache_ops.hpp"
 #include "decode.hpp"
+#include "extend.hpp"
 #include "status.hpp"
 
 namespace pkv {
@@ -246,6 +247,69 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
   return from_hip(pkv::launch_decode(a, cache->dtype, cache->head_dim, cache->block_size, group,
                                      (hipStream_t)stream),
                   "paged_attn_decode launch");
+}
+
+PKV_EXPORT pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache, const void* v_cache,
+                                            const pkv_cache_desc* cache, const int32_t* block_table,
+                                            int32_t table_width, const int32_t* seq_lens,
+                                            const int32_t* query_start, int32_t num_seqs,
+                                            int32_t num_tokens, int32_t q_heads,
+                                            int32_t max_query_len, float scale, void* out,
+                                            void* stream) {
+  pkv_status st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0)
+    return fail(PKV_ERR_SHAPE, "num_seqs, num_tokens and max_query_len must be >= 0");
+  if (q_heads < 1 || q_heads % cache->kv_heads)
+    return fail(PKV_ERR_SHAPE, "q_heads (%d) must be a positive multiple of kv_heads (%d)",
+                (int)q_heads, (int)cache->kv_heads);
+  const int group = q_heads / cache->kv_heads;
+  if (!pkv::extend_supported(cache->dtype, cache->head_dim, cache->block_size, group))
+    return fail(PKV_ERR_UNSUPPORTED, "extend attention supports bf16 caches with head_dim 128, "
+                "block_size 16 or 32 and G in {1, 2, 4, 8} (got dtype %d, head_dim %d, "
+                "block_size %d, G %d)", (int)cache->dtype, (int)cache->head_dim,
+                (int)cache->block_size, group);
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
+  if (table_width < 1) return fail(PKV_ERR_SHAPE, "table_width must be >= 1");
+  if ((int64_t)table_width * cache->block_size > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "table_width * block_size exceeds the int32 token range");
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start || !out)
+    return fail(PKV_ERR_NULL, "q, k_cache, v_cache, block_table, seq_lens, query_start and out "
+                "must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  const int64_t row_bytes = (int64_t)cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype);
+  const int64_t block_bytes = row_bytes * cache->block_size;
+  if (block_bytes > UINT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "a block of %lld bytes exceeds 4 GiB", (long long)block_bytes);
+  const int64_t tokens_per_wg = pkv::kExtendCols / group;
+  const int64_t q_tiles = (max_query_len + tokens_per_wg - 1) / tokens_per_wg;
+  const int64_t units = (int64_t)num_seqs * cache->kv_heads * q_tiles;
+  if (units + 8 > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)units);
+
+  pkv::ExtendArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.out = out;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.query_start = query_start;
+  a.num_blocks = cache->num_blocks;
+  a.table_width = table_width;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.q_heads = q_heads;
+  a.kv_heads = cache->kv_heads;
+  a.max_query_len = max_query_len;
+  a.q_tiles = (int32_t)q_tiles;
+  a.units = (int32_t)units;
+  a.row_bytes = (uint32_t)row_bytes;
+  a.block_bytes = (uint32_t)block_bytes;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return from_hip(pkv::launch_extend(a, cache->block_size, group, (hipStream_t)stream),
+                  "paged_attn_extend launch");
 }
 
 PKV_EXPORT pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pairs, void* k_cache,

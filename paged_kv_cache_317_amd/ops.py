@@ -119,6 +119,36 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale, max_seq
     return out
 
 
+def paged_attn_extend(q, k_cache, v_cache, block_table, seq_lens, query_start, scale,
+                      max_query_len, out=None):
+    """Causal attention of each sequence's new tokens (prefill or chunked
+    extend) over the paged cache.  ``q`` and ``out`` are packed
+    ``[T, q_heads, head_dim]``; sequence ``s`` owns rows
+    ``query_start[s] .. query_start[s + 1] - 1``.  ``max_query_len`` is a
+    host-side bound on those counts.  Returns ``out``."""
+    desc = _check_caches(k_cache, v_cache)
+    dev = k_cache.device
+    if q.dim() != 3:
+        raise ValueError("q must be [num_tokens, q_heads, head_dim]")
+    T, Hq, D = q.shape
+    _require(q, "q", dev, k_cache.dtype, (T, Hq, desc.head_dim))
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, table_width]")
+    S = block_table.shape[0]
+    _require(block_table, "block_table", dev, torch.int32)
+    _require(seq_lens, "seq_lens", dev, torch.int32, (S,))
+    _require(query_start, "query_start", dev, torch.int32, (S + 1,))
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", dev, q.dtype, q.shape)
+    with torch.cuda.device(dev):
+        check(lib().pkv_paged_attn_extend(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), _ptr(query_start), S, T, Hq,
+            int(max_query_len), float(scale), _ptr(out), _stream(dev)))
+    return out
+
+
 def paged_block_copy(pairs, k_cache, v_cache):
     """Copy whole blocks ``pairs[i, 0] -> pairs[i, 1]`` in both caches."""
     desc = _check_caches(k_cache, v_cache)
