@@ -169,6 +169,7 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,
  *                written whatever it holds
  *   max_query_len host-side bound on every n (sizes the grid); query rows
  *                j >= max_query_len of a sequence are not written
+ *   scale        softmax scale, positive and finite (PKV_ERR_SHAPE otherwise)
  * No workspace.  Supported: bf16 caches with head_dim 128, block_size 16 or
  * 32, G in {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.
  */

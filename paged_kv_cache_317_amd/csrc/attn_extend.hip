@@ -17,7 +17,8 @@
 //   column    one (query token, query head) pair of one kv head; the G heads
 //             of a token are adjacent columns
 //   workgroup 128 columns (128 / G tokens) of one sequence and kv head;
-//             four waves of 32 columns (two 16-column MFMA groups each)
+//             four waves of 32 columns (two 16-column MFMA groups each;
+//             the group count is a build option)
 //   tile      64 consecutive key positions, staged in LDS once per
 //             workgroup and read by all four waves
 // Workgroups are ordered so that the query tiles of one (sequence, kv head)
@@ -29,9 +30,12 @@
 //                 group the N columns (B operand, held in registers for the
 //                 whole call).  Lane (r, c) gets keys 4r..4r+3 of column c
 //                 for each 16-key block.
-//   softmax       online, base 2, scale folded with log2 e; the tile max of
-//                 a column is an in-lane max plus two row swaps; the causal
-//                 and length mask is applied only on tiles that need it.
+//   softmax       online, base 2, scale folded with log2 e into one fma per
+//                 weight; the tile max of a column is an in-lane max plus
+//                 two row swaps; the running max moves only when passed by
+//                 more than 8 (log2 units), so O is rarely rescaled; the
+//                 causal and length mask is applied only on tiles that need
+//                 it.
 //   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16 with the 32 keys of two 16-key
 //                 blocks as the K dimension in the order that matches the
 //                 logits' lane layout: P stays in its lanes (rounded to
@@ -52,13 +56,56 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kD = 128;                  // head_dim
 constexpr int kKeys = 64;                // key positions per tile
-constexpr int kThreads = 256;
-constexpr int kGroups = 2;               // 16-column groups per wave
-constexpr int kKRow = kD * 2 + 16;       // padded LDS row of the K tile (bytes)
-constexpr int kVRow = kD * 2 + 32;       // padded LDS row of the V tile (bytes)
+constexpr int kWaves = PKV_EXTEND_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStep = kThreads / 16;     // K/V rows one pass of the workgroup loads
+constexpr int kRowsPerThread = kKeys / kStep;
+constexpr int kGroups = PKV_EXTEND_GROUPS;   // 16-column groups per wave
+constexpr int kWaveCols = 16 * kGroups;
+#ifndef PKV_EXTEND_KPAD
+#define PKV_EXTEND_KPAD 16
+#endif
+#ifndef PKV_EXTEND_VPAD
+#define PKV_EXTEND_VPAD 32
+#endif
+constexpr int kKRow = kD * 2 + PKV_EXTEND_KPAD;   // padded LDS row of the K tile (bytes)
+constexpr int kVRow = kD * 2 + PKV_EXTEND_VPAD;   // padded LDS row of the V tile (bytes)
 constexpr int kKTile = kKeys * kKRow;
+constexpr float kLazyLog2 = 8.f;         // running-max slack before O is rescaled
 constexpr int kVTile = kKeys * kVRow;
-static_assert(kExtendCols == 4 * 16 * kGroups, "four waves of kGroups 16-column groups");
+static_assert(kExtendCols == kWaves * 16 * kGroups, "kWaves waves of kGroups 16-column groups");
+static_assert(kKeys % kStep == 0, "whole rows per thread");
+
+// Ping-pong schedule between the two halves of an 8-wave workgroup (three
+// LDS tile buffers), or one wave-synchronous loop (two buffers).
+#ifndef PKV_EXTEND_PINGPONG
+#define PKV_EXTEND_PINGPONG 0
+#endif
+static_assert(!PKV_EXTEND_PINGPONG || kWaves == 8, "ping-pong needs two waves per SIMD");
+constexpr int kBufs = PKV_EXTEND_PINGPONG ? 3 : 2;
+
+// Unit order: 0 = the units of one XCD contiguous, 1 = query tiles from the
+// last down, kv head fastest (the kv heads of a tile spread over the XCDs,
+// one kv head's tiles stay on one XCD when kv_heads is a multiple of 8).
+#ifndef PKV_EXTEND_ORDER
+#define PKV_EXTEND_ORDER 2
+#endif
+#ifndef PKV_EXTEND_WAVES_PER_EU
+#define PKV_EXTEND_WAVES_PER_EU 2
+#endif
+
+// Optional wave priority: raised while a wave issues its matrix products,
+// so that the scheduler keeps the matrix pipe fed from whichever wave is in
+// that phase.
+#ifndef PKV_EXTEND_PRIO
+#define PKV_EXTEND_PRIO 0
+#endif
+__device__ __forceinline__ void mfma_phase(bool on) {
+  if (PKV_EXTEND_PRIO) {
+    if (on) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+}
 
 __device__ __forceinline__ bf16x8_t cat(bf16x4_t lo, bf16x4_t hi) {
   return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -70,19 +117,17 @@ __device__ __forceinline__ bf16x4_t tr_read(const char* lds, int byte_off) {
 }
 
 template <int BS, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_EXTEND_WAVES_PER_EU)))
 void extend_kernel(ExtendArgs a) {
   static_assert(BS == 16 || BS == 32, "block_size 16 or 32");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1, 2, 4, 8}");
   constexpr int kTokens = kExtendCols / G;       // query tokens per workgroup
-  constexpr int kEntries = kKeys / BS;           // table entries per tile
-  constexpr int kRowsPerThread = kKeys * 16 / kThreads;   // 16-byte chunks per thread per tile
-  static_assert(kRowsPerThread == 4, "four rows per thread per tile");
 
-  __shared__ __attribute__((aligned(16))) char s_k[2][kKTile];
-  __shared__ __attribute__((aligned(16))) char s_v[2][kVTile];
+  __shared__ __attribute__((aligned(16))) char s_k[kBufs][kKTile];
+  __shared__ __attribute__((aligned(16))) char s_v[kBufs][kVTile];
   __shared__ int s_first_bad;
 
+#if PKV_EXTEND_ORDER == 0
   const int per_xcd = (a.units + 7) / 8;
   const int unit = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (unit >= a.units) return;
@@ -90,6 +135,26 @@ void extend_kernel(ExtendArgs a) {
   const int rest = unit / a.q_tiles;
   const int g = rest % a.kv_heads;
   const int s = rest / a.kv_heads;
+#elif PKV_EXTEND_ORDER == 1
+  const int unit = (int)blockIdx.x;
+  if (unit >= a.units) return;
+  const int g = unit % a.kv_heads;
+  const int rest = unit / a.kv_heads;
+  const int s = rest % a.num_seqs;
+  const int qt = a.q_tiles - 1 - rest / a.num_seqs;  // later (longer) query tiles first
+#else
+  // (sequence, kv head) pairs go round-robin over the XCDs; on its XCD a
+  // pair's query tiles are consecutive, so they run side by side and read
+  // the pair's keys and values through the same L2.
+  const int unit = (int)blockIdx.x;
+  const int xcd = unit % 8;
+  const int local = unit / 8;
+  const int pair = (local / a.q_tiles) * 8 + xcd;
+  const int qt = a.q_tiles - 1 - local % a.q_tiles;  // later (longer) query tiles first
+  const int g = pair % a.kv_heads;
+  const int s = pair / a.kv_heads;
+  if (s >= a.num_seqs) return;
+#endif
 
   const int q0 = a.query_start[s];
   const int n_raw = a.query_start[s + 1] - q0;
@@ -133,7 +198,7 @@ void extend_kernel(ExtendArgs a) {
   u32x4_t qv[kGroups][4];
 #pragma unroll
   for (int cg = 0; cg < kGroups; ++cg) {
-    const int col = 32 * wave + 16 * cg + lc;
+    const int col = kWaveCols * wave + 16 * cg + lc;
     const int j = j0 + col / G;
     cvalid[cg] = j < j1;
     const int jc = min(j, j1 - 1);
@@ -144,9 +209,9 @@ void extend_kernel(ExtendArgs a) {
     for (int ks = 0; ks < 4; ++ks)
       qv[cg][ks] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * rg);
   }
-  const bool wave_active = j0 + (32 * wave) / G < j1;
-  const int qmin_w = ctx + min(j0 + (32 * wave) / G, j1 - 1);
-  const int qmax_w = ctx + min(j0 + (32 * wave + 31) / G, j1 - 1);
+  const bool wave_active = j0 + (kWaveCols * wave) / G < j1;
+  const int qmin_w = ctx + min(j0 + (kWaveCols * wave) / G, j1 - 1);
+  const int qmax_w = ctx + min(j0 + (kWaveCols * wave + kWaveCols - 1) / G, j1 - 1);
 
   // Tile loader: thread t moves chunk t % 16 of rows t / 16 + 16 i.
   const int lchunk = threadIdx.x & 15;
@@ -155,18 +220,24 @@ void extend_kernel(ExtendArgs a) {
   const char* kcache = reinterpret_cast<const char*>(a.k_cache);
   const char* vcache = reinterpret_cast<const char*>(a.v_cache);
 
-  // Table entries of a tile (vector loads, so that waiting for them never
-  // holds up the LDS traffic of the tile being computed).
-  auto fetch_entries = [&](int tile, int (&e)[kEntries]) {
+  // Table entries of this thread's rows of a tile (the same for a whole
+  // wave; vector loads, so that waiting for them never holds up the LDS
+  // traffic of the tile being computed).
+  // A wave's 64 threads load 4 consecutive rows (row base 4 * wave), which
+  // lie in one 16-row block, so the entry index is wave-uniform.
+  const int wave_row = uniform_int(4 * wave);
+  auto fetch_entries = [&](int tile, int (&e)[kRowsPerThread]) {
 #pragma unroll
-    for (int k = 0; k < kEntries; ++k) e[k] = trow[min(tile * kEntries + k, last_blk)];
+    for (int i = 0; i < kRowsPerThread; ++i)
+      e[i] = trow[min((tile * kKeys + wave_row + kStep * i) / BS, last_blk)];
   };
-  auto load_tile = [&](const int (&e)[kEntries], u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
+  auto load_tile = [&](const int (&e)[kRowsPerThread], u32x4_t (&kr)[kRowsPerThread],
+                       u32x4_t (&vr)[kRowsPerThread]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t phys = (uint32_t)uniform_int(e[(16 * i) / BS]);
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const uint32_t phys = (uint32_t)uniform_int(e[i]);
       const uint64_t base = (uint64_t)phys * a.block_bytes;
-      uint32_t off = (uint32_t)((lrow + (16 * i) % BS) * a.row_bytes) + lane_off;
+      uint32_t off = (uint32_t)(((lrow + kStep * i) % BS) * a.row_bytes) + lane_off;
       asm volatile("" : "+v"(off));
       kr[i] = *reinterpret_cast<const u32x4_t*>(kcache + base + off);
       vr[i] = *reinterpret_cast<const u32x4_t*>(vcache + base + off);
@@ -174,30 +245,36 @@ void extend_kernel(ExtendArgs a) {
   };
   // Rows at or past kv_hi (only in the last tile) are stored as zeros: they
   // may be unused slots holding any bits.
-  auto store_tile = [&](int tile, int buf, u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
+  auto store_tile = [&](int tile, int buf, u32x4_t (&kr)[kRowsPerThread],
+                        u32x4_t (&vr)[kRowsPerThread]) {
     const int t0 = tile * kKeys;
-    if (t0 + kKeys > kv_hi) {
+    if (uniform_int(t0 + kKeys > kv_hi ? 1 : 0)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (t0 + lrow + 16 * i >= kv_hi) {
+      for (int i = 0; i < kRowsPerThread; ++i) {
+        if (t0 + lrow + kStep * i >= kv_hi) {
           kr[i] = u32x4_t{0u, 0u, 0u, 0u};
           vr[i] = u32x4_t{0u, 0u, 0u, 0u};
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4_t*>(&s_k[buf][(lrow + 16 * i) * kKRow + 16 * lchunk]) = kr[i];
-      *reinterpret_cast<u32x4_t*>(&s_v[buf][(lrow + 16 * i) * kVRow + 16 * lchunk]) = vr[i];
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      *reinterpret_cast<u32x4_t*>(&s_k[buf][(lrow + kStep * i) * kKRow + 16 * lchunk]) = kr[i];
+      *reinterpret_cast<u32x4_t*>(&s_v[buf][(lrow + kStep * i) * kVRow + 16 * lchunk]) = vr[i];
     }
   };
 
-  float m_run[kGroups], l_run[kGroups];
+  // Running max per column; the softmax denominator accumulates in the
+  // matrix pipe as the product of an all-ones operand with the weights
+  // (every element of lsum[cg] holds the column's sum of the bf16 weights,
+  // the same weights the value sum uses).
+  float m_run[kGroups];
+  f32x4_t lsum[kGroups];
   f32x4_t ot[kGroups][kD / 16];
 #pragma unroll
   for (int cg = 0; cg < kGroups; ++cg) {
     m_run[cg] = -INFINITY;
-    l_run[cg] = 0.f;
+    lsum[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) ot[cg][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -206,12 +283,15 @@ void extend_kernel(ExtendArgs a) {
   const int ka_lane = lc * kKRow + 16 * rg;                        // K row lc, chunk rg
   const int tr_lane = (4 * rg + (lc >> 2)) * kVRow + 8 * (lc & 3);  // V transpose read
 
-  auto compute = [&](int tile, int buf) {
-    const int t0 = tile * kKeys;
-    if (!wave_active || t0 > qmax_w) return;
+  // The three stages of a tile.  A wave whose columns all sit before the
+  // tile (tile_active false) skips all three.
+  f32x4_t sacc[kGroups][4];   // logits of the tile between qk and softmax
+  bf16x4_t pb[kGroups][4];    // its weights between softmax and pv
+  auto tile_active = [&](int tile) { return wave_active && tile * kKeys <= qmax_w; };
+
+  auto qk = [&](int buf) {
     const char* kt = s_k[buf];
-    const char* vt = s_v[buf];
-    f32x4_t sacc[kGroups][4];
+    mfma_phase(true);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       u32x4_t ka[4];
@@ -229,46 +309,63 @@ void extend_kernel(ExtendArgs a) {
         sacc[cg][kb] = acc;
       }
     }
-    const bool need_mask = (t0 + kKeys - 1 > qmin_w) || (t0 + kKeys > kv_hi);
-    bf16x4_t pb[kGroups][4];
+    mfma_phase(false);
+  };
+
+  auto softmax = [&](int tile) {
+    const int t0 = tile * kKeys;
+    // Only tiles that reach past the wave's first query position, or past
+    // the readable keys, need the mask (a wave-uniform test).
+    const bool need_mask =
+        uniform_int((t0 + kKeys - 1 > qmin_w) || (t0 + kKeys > kv_hi) ? 1 : 0) != 0;
+    if (need_mask) {
+#pragma unroll
+      for (int cg = 0; cg < kGroups; ++cg) {
+        // keys 16 kb + i of this lane are visible while below `lim`
+        const int lim = min(qpos[cg] + 1, kv_hi) - t0 - 4 * rg;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * kb + i >= lim) sacc[cg][kb][i] = -INFINITY;
+      }
+    }
 #pragma unroll
     for (int cg = 0; cg < kGroups; ++cg) {
-      float x[4][4];
+      // The scale is positive, so the tile max is taken on the raw logits.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[cg][kb][i] * a.scale_log2;
-          if (need_mask) {
-            const int kp = t0 + 16 * kb + 4 * rg + i;
-            if (kp > qpos[cg] || kp >= kv_hi) v = -INFINITY;
-          }
-          x[kb][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m_run[cg], mx);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[cg][kb][i]);
+      mx = max_xor32(max_xor16(mx)) * a.scale_log2;
+      // Lazy rescaling: the running max only moves when the tile max passes
+      // it by more than kLazyLog2, so the weights stay below 2^kLazyLog2 and
+      // most tiles skip the rescale of O.
+      const float m_old = m_run[cg];
+      const float m_new = mx > m_old + kLazyLog2 ? mx : m_old;
       // A column with nothing visible yet keeps weight 0 everywhere.
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(x[kb][i] - m_use);
-          psum += p;
-          pb[cg][kb][i] = (__bf16)p;
-        }
-      }
-      l_run[cg] = l_run[cg] * alpha + psum;
-      m_run[cg] = m_new;
-      if (__any(alpha != 1.f)) {
+      if (__any(m_new != m_old)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        lsum[cg] *= alpha;
 #pragma unroll
         for (int db = 0; db < kD / 16; ++db) ot[cg][db] *= alpha;
       }
+      m_run[cg] = m_new;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pb[cg][kb][i] =
+              (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[cg][kb][i], a.scale_log2, -m_use));
+      }
     }
+  };
+
+  auto pv = [&](int buf) {
+    const char* vt = s_v[buf];
+    mfma_phase(true);
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
@@ -281,16 +378,59 @@ void extend_kernel(ExtendArgs a) {
           ot[cg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               av, cat(pb[cg][2 * kp], pb[cg][2 * kp + 1]), ot[cg][db], 0, 0, 0);
       }
+      const bf16x8_t ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                             (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+      for (int cg = 0; cg < kGroups; ++cg)
+        lsum[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            ones, cat(pb[cg][2 * kp], pb[cg][2 * kp + 1]), lsum[cg], 0, 0, 0);
     }
+    mfma_phase(false);
   };
 
   if (ntiles > 0) {
-    int ent[kEntries];
-    u32x4_t kr[4], vr[4];
+    int ent[kRowsPerThread];
+    u32x4_t kr[kRowsPerThread], vr[kRowsPerThread];
     fetch_entries(0, ent);
     load_tile(ent, kr, vr);
     fetch_entries(1, ent);
     store_tile(0, 0, kr, vr);
+#if PKV_EXTEND_PINGPONG
+    // Two halves of the workgroup (waves 0-3 and 4-7, one of each per SIMD)
+    // run half a tile apart.  Phase p ends with a barrier; in it one half
+    // issues matrix products (PV of tile j-1 and QK of tile j) while the
+    // other computes the softmax of its current tile, so each SIMD always
+    // has one wave feeding the matrix pipe.  Tile t is stored in LDS buffer
+    // t % 3 during phase 2t - 2 (its loads were issued two phases earlier);
+    // the buffer's previous tile was last read in phase 2t - 3.
+    if (ntiles > 1) {
+      load_tile(ent, kr, vr);
+      fetch_entries(2, ent);
+    }
+    __syncthreads();
+    const int half = wave >> 2;
+    for (int p = 0; p < 2 * ntiles + 2; ++p) {
+      if ((p & 1) == 0) {
+        const int t = p / 2 + 1;
+        if (t < ntiles) {
+          store_tile(t, t % 3, kr, vr);
+          if (t + 1 < ntiles) {
+            load_tile(ent, kr, vr);
+            fetch_entries(t + 2, ent);
+          }
+        }
+      }
+      const bool x_phase = ((p & 1) == 0) == (half == 0);
+      const int j = half == 0 ? p >> 1 : (p - 1) >> 1;
+      if (x_phase) {
+        if (j >= 1 && tile_active(j - 1)) pv((j - 1) % 3);
+        if (j < ntiles && tile_active(j)) qk(j % 3);
+      } else if (j >= 0 && j < ntiles && tile_active(j)) {
+        softmax(j);
+      }
+      __syncthreads();
+    }
+#else
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const bool more = t + 1 < ntiles;
@@ -298,17 +438,22 @@ void extend_kernel(ExtendArgs a) {
         load_tile(ent, kr, vr);
         fetch_entries(t + 2, ent);
       }
-      compute(t, t & 1);
+      if (tile_active(t)) {
+        qk(t & 1);
+        softmax(t);
+        pv(t & 1);
+      }
       if (more) store_tile(t + 1, (t + 1) & 1, kr, vr);
       __syncthreads();
     }
+#endif
   }
 
 #pragma unroll
   for (int cg = 0; cg < kGroups; ++cg) {
-    const float l_tot = sum_xor32(sum_xor16(l_run[cg]));
+    const float l_tot = lsum[cg][0];
     if (cvalid[cg]) {
-      const int col = 32 * wave + 16 * cg + lc;
+      const int col = kWaveCols * wave + 16 * cg + lc;
       const int j = j0 + col / G;
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       __bf16* out = reinterpret_cast<__bf16*>(a.out) +
@@ -326,8 +471,13 @@ void extend_kernel(ExtendArgs a) {
 
 template <int BS, int G>
 hipError_t launch_one(const ExtendArgs& a, hipStream_t stream) {
-  const int per_xcd = (a.units + 7) / 8;
-  hipLaunchKernelGGL((extend_kernel<BS, G>), dim3(8 * per_xcd), dim3(kThreads), 0, stream, a);
+  // Order 2 maps unit u to pair (u / 8 / q_tiles) * 8 + u % 8: the grid
+  // covers every pair index below num_seqs * kv_heads rounded up to 8.
+  const int pairs8 = 8 * ((a.num_seqs * a.kv_heads + 7) / 8);
+  const int grid = PKV_EXTEND_ORDER == 0   ? 8 * ((a.units + 7) / 8)
+                   : PKV_EXTEND_ORDER == 1 ? a.units
+                                           : pairs8 * a.q_tiles;
+  hipLaunchKernelGGL((extend_kernel<BS, G>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -29,9 +29,16 @@ struct ExtendArgs {
   float scale_log2;            // scale * log2(e)
 };
 
+// Waves per workgroup and 16-column MFMA groups per wave.
+#ifndef PKV_EXTEND_WAVES
+#define PKV_EXTEND_WAVES 8
+#endif
+#ifndef PKV_EXTEND_GROUPS
+#define PKV_EXTEND_GROUPS 2
+#endif
 // Query columns (token, head) one workgroup covers; a workgroup holds
 // kExtendCols / G query tokens of one sequence.
-constexpr int kExtendCols = 128;
+constexpr int kExtendCols = PKV_EXTEND_WAVES * 16 * PKV_EXTEND_GROUPS;
 
 bool extend_supported(int dtype, int head_dim, int block_size, int group);
 hipError_t launch_extend(const ExtendArgs& a, int block_size, int group, hipStream_t stream);

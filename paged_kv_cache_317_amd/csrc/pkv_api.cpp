@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -269,6 +270,8 @@ PKV_EXPORT pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache, 
                 "block_size 16 or 32 and G in {1, 2, 4, 8} (got dtype %d, head_dim %d, "
                 "block_size %d, G %d)", (int)cache->dtype, (int)cache->head_dim,
                 (int)cache->block_size, group);
+  if (!(scale > 0.f) || !(scale < INFINITY))
+    return fail(PKV_ERR_SHAPE, "scale must be positive and finite");
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
   if (table_width < 1) return fail(PKV_ERR_SHAPE, "table_width must be >= 1");
   if ((int64_t)table_width * cache->block_size > INT32_MAX)
@@ -285,8 +288,10 @@ PKV_EXPORT pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache, 
   const int64_t tokens_per_wg = pkv::kExtendCols / group;
   const int64_t q_tiles = (max_query_len + tokens_per_wg - 1) / tokens_per_wg;
   const int64_t units = (int64_t)num_seqs * cache->kv_heads * q_tiles;
-  if (units + 8 > INT32_MAX)
-    return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)units);
+  // The launch may round the (sequence, kv head) pairs up to a multiple of 8.
+  const int64_t grid = ((int64_t)num_seqs * cache->kv_heads + 7) / 8 * 8 * q_tiles;
+  if (grid > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
 
   pkv::ExtendArgs a;
   a.q = q;
