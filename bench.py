@@ -77,26 +77,39 @@ def copy_probe(gib, steps, warmup):
     return 0
 
 
-PROFILE = os.path.join(ROOT, "profiles", "paged_attn_decode_c3_gqa4k_bf16.md")
 DECODE_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_decode.hip",
                   "paged_kv_cache_317_amd/csrc/device_common.hpp",
                   "paged_kv_cache_317_amd/csrc/decode.hpp"]
+EXTEND_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_extend.hip",
+                  "paged_kv_cache_317_amd/csrc/device_common.hpp",
+                  "paged_kv_cache_317_amd/csrc/extend.hpp"]
+# Counter summaries per (kernel, workload): the HBM bytes per launch they
+# record count only while the kernel sources hash to the recorded value.
+PROFILES = {
+    DEFAULT_WORKLOAD: ("paged_attn_decode_c3_gqa4k_bf16.md", DECODE_SOURCES),
+    "x3_extend_bf16": ("paged_attn_extend_x3_extend_bf16.md", EXTEND_SOURCES),
+}
 
 
 def profiled_traffic(workload):
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when there is none for this workload or the kernel sources changed since."""
+    """HBM bytes per launch of the workload's attention kernel from the
+    committed counter summary, or None when there is none for this workload
+    or the kernel sources changed since it was taken."""
     import hashlib
     import re
-    if workload != DEFAULT_WORKLOAD or not os.path.exists(PROFILE):
+    if workload not in PROFILES:
         return None
-    text = open(PROFILE).read()
+    name, sources = PROFILES[workload]
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
     sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     traffic = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
     if not sha or not traffic:
         return None
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in sources:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return int(traffic.group(1)) if h.hexdigest() == sha.group(1) else None
 
@@ -411,7 +424,7 @@ def extend_bench(args):
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "flops_per_launch": flops,
             "kv_bytes_per_launch": kv_bytes + io_bytes,
-            "traffic": None,
+            "traffic": profiled_traffic(cfg.name),
         },
         "cpu_baseline": cpu,
     }
