@@ -116,13 +116,6 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_s
 #ifndef PKV_DECODE_WAVES_PER_EU
 #define PKV_DECODE_WAVES_PER_EU 4
 #endif
-// Tiles in flight per wave while one is computed (register sets: 1 or 2).
-#ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 1
-#endif
-constexpr int kDepth = PKV_DECODE_DEPTH;
-static_assert(kDepth == 1 || kDepth == 2, "one or two register sets");
-
 template <typename T, int D, int BS, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
 void decode_partition_kernel(DecodeArgs a) {
@@ -136,6 +129,9 @@ void decode_partition_kernel(DecodeArgs a) {
   // transpose reads of a 16-lane group hit distinct banks.
   constexpr int kVRow = D * 2 + 32;
   constexpr int kVTileBytes = kBf16 ? kTile * kVRow : 16;
+  // Staging rows of the split states in the V tile: D bf16 + 16 bytes of padding.
+  constexpr int kStageRowBytes = 2 * D + 16;
+  static_assert(!kBf16 || G * kStageRowBytes <= kVTileBytes, "split staging fits the V tile");
   // bf16 K tile: rows padded by 16 bytes so that the 16 rows one operand read
   // touches fall in distinct banks.
   constexpr int kKRow = D * 2 + 16;
@@ -155,14 +151,15 @@ void decode_partition_kernel(DecodeArgs a) {
   int unit = blockIdx.x;
   const int grp = unit % groups;
   unit /= groups;
-  const int part = unit % a.num_parts;
-  const int s = unit / a.num_parts;
+  const int chunk = unit % a.num_chunks;           // parts_per_unit consecutive partitions
+  const int s = unit / a.num_chunks;
   const int g = grp * a.heads_per_wg + wave;
 
   const int L = clamp_len(a, s, BS);
-  const int t0 = part * a.part_tokens;
+  const int span = a.part_tokens * a.parts_per_unit;
+  const int t0 = chunk * span;
   if (a.num_parts > 1 && t0 >= L) return;          // uniform over the workgroup
-  int t1 = min(L, t0 + a.part_tokens);
+  int t1 = min(L, t0 + span);
   const int nblk = max(t1 - t0, 0) / BS + ((max(t1 - t0, 0) % BS) != 0);
   const int j0 = t0 / BS;
 
@@ -372,58 +369,111 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // kDepth register sets, each refilled as soon as its tile is staged: while
-  // tile t is computed, tiles t+1 .. t+kDepth are in flight.  Loads past the
-  // last tile re-read it (an L2 hit) so that every iteration issues the same
-  // loads.
-  const int ntiles = (ntok + kTile - 1) / kTile;
-  const int nfull = ntok / kTile;
-  if (ntiles > 0) {
-    const int last = ntiles - 1;
-    if constexpr (kDepth == 1) {
-      u32x4_t kr[4], vr[4];
-      load_tile(0, kr, vr);
-      for (int t = 0; t < ntiles; ++t)
-        process(t0 + t * kTile, t == nfull, kr, vr, [&] { load_tile(min(t + 1, last), kr, vr); });
-    } else {
-      u32x4_t ka[4], va[4], kb[4], vb[4];
-      load_tile(0, ka, va);
-      load_tile(min(1, last), kb, vb);
-      for (int t = 0; t < ntiles; t += 2) {
-        process(t0 + t * kTile, t == nfull, ka, va, [&] { load_tile(min(t + 2, last), ka, va); });
-        if (t + 1 >= ntiles) break;
-        process(t0 + (t + 1) * kTile, t + 1 == nfull, kb, vb,
-                [&] { load_tile(min(t + 3, last), kb, vb); });
-      }
-    }
-  }
-
-  // Sum the four row groups' shares of the softmax denominator.
-  const float l_tot = sum_xor32(sum_xor16(l_run));
-
-  if constexpr (kBf16) {
-    // Lane (r, c) owns dims 16dt + 4r .. +3 of head c.
-    if (lc < G) {
-      const int64_t orow = (int64_t)s * a.q_heads + hq0 + lc;
-      if (a.num_parts == 1) {
+  // Split calls: this wave's unnormalised state (running max in log2 units,
+  // sum, o) of partition p goes to the workspace, and the state restarts.
+  auto emit_partial = [&](int p) {
+    const float l_tot = sum_xor32(sum_xor16(l_run));
+    // Partition p's states of this wave's G heads are adjacent in the
+    // workspace ([S, P, Hq, ...] order): G * D floats of o, G (m, l) pairs.
+    const int64_t row0 = ((int64_t)s * a.num_parts + p) * a.q_heads + hq0;
+    if constexpr (kBf16) {
+      // bf16 caches: the partition's output is stored normalised (o / l) in
+      // bf16, next to its max and sum in fp32.  It goes through this wave's
+      // V tile (free between tiles) so that the workspace is written in
+      // whole runs, 16 bytes per lane, with non-temporal stores.
+      char* st = vt;
+      if (lc < G) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        __bf16* out = reinterpret_cast<__bf16*>(a.out) + orow * D + 4 * rg;
 #pragma unroll
         for (int dt = 0; dt < kDimTiles; ++dt) {
           bf16x4_t w;
 #pragma unroll
           for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[dt][i] * inv);
-          *reinterpret_cast<bf16x4_t*>(out + 16 * dt) = w;
+          *reinterpret_cast<bf16x4_t*>(st + lc * kStageRowBytes + 2 * (16 * dt + 4 * rg)) = w;
         }
-      } else {
-        const int64_t slot = orow * a.num_parts + part;
-        float* po = a.part_o + slot * D + 4 * rg;
+        if (rg == 0)
+          *reinterpret_cast<float2*>(a.part_ml + 2 * (row0 + lc)) = float2{m_run, l_tot};
+      }
+      __builtin_amdgcn_wave_barrier();
+      __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + row0 * D;
 #pragma unroll
-        for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4_t*>(po + 16 * dt) = ot[dt];
-        if (rg == 0) {
-          a.part_ml[2 * slot] = m_run;
-          a.part_ml[2 * slot + 1] = l_tot;
+      for (int idx = 8 * lane; idx < G * D; idx += 8 * kWave)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4_t*>(st + (idx / D) * kStageRowBytes + 2 * (idx % D)),
+            reinterpret_cast<u32x4_t*>(po + idx));
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int dt = 0; dt < kDimTiles; ++dt) ot[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+      static_for<G>([&](auto H) {
+        constexpr int h = H;
+        const float l_h = read_lane(l_tot, h);
+        const float m_h = read_lane(m_run, h);
+        float oh[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          oh[e] = sum_xor32(sum_xor16(o[h][e]));
+          o[h][e] = 0.f;
         }
+        if (rg == (h & 3)) {
+          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.part_o) + (row0 + h) * D + lc * E) =
+              f32x4_t{oh[0], oh[1], oh[2], oh[3]};
+          if (lc == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * (row0 + h)) = float2{m_h, l_h};
+        }
+      });
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+
+  // One register set, refilled as soon as its tile is staged: while tile t
+  // is computed, tile t+1 is in flight.  Loads past the last tile re-read it
+  // (an L2 hit) so that every iteration issues the same loads.  A split
+  // wave may walk several consecutive partitions: the loads run straight
+  // through, and the state is emitted at every partition boundary.
+  const bool split = a.num_parts > 1;
+  const int p_first = chunk * a.parts_per_unit;
+  int p_next = p_first;                            // first partition not emitted yet
+  const int ntiles = (ntok + kTile - 1) / kTile;
+  const int nfull = ntok / kTile;
+  if (ntiles > 0) {
+    const int last = ntiles - 1;
+    u32x4_t kr[4], vr[4];
+    load_tile(0, kr, vr);
+    for (int t = 0; t < ntiles; ++t) {
+      process(t0 + t * kTile, t == nfull, kr, vr, [&] { load_tile(min(t + 1, last), kr, vr); });
+      const int tend = t0 + (t + 1) * kTile;
+      if (split && (t == last || tend % a.part_tokens == 0)) {
+        const int p = (tend - 1) / a.part_tokens;
+        emit_partial(p);
+        p_next = p + 1;
+      }
+    }
+  }
+
+  if (split) {
+    // Partitions of this wave's span that hold no readable token (past a
+    // table entry outside the pool) carry an empty state.
+    const int p_end = min(p_first + a.parts_per_unit, (L + a.part_tokens - 1) / a.part_tokens);
+    for (int p = p_next; p < p_end; ++p) emit_partial(p);
+    return;
+  }
+
+  // Unsplit: sum the four row groups' shares of the softmax denominator and
+  // store the normalised rows.
+  const float l_tot = sum_xor32(sum_xor16(l_run));
+  if constexpr (kBf16) {
+    // Lane (r, c) owns dims 16dt + 4r .. +3 of head c.
+    if (lc < G) {
+      const int64_t orow = (int64_t)s * a.q_heads + hq0 + lc;
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* out = reinterpret_cast<__bf16*>(a.out) + orow * D + 4 * rg;
+#pragma unroll
+      for (int dt = 0; dt < kDimTiles; ++dt) {
+        bf16x4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[dt][i] * inv);
+        *reinterpret_cast<bf16x4_t*>(out + 16 * dt) = w;
       }
     }
   } else {
@@ -435,22 +485,11 @@ void decode_partition_kernel(DecodeArgs a) {
     static_for<G>([&](auto H) {
       constexpr int h = H;
       const float l_h = read_lane(l_tot, h);
-      const float m_h = read_lane(m_run, h);
       if (rg == (h & 3)) {
         const int64_t orow = (int64_t)s * a.q_heads + hq0 + h;
-        if (a.num_parts == 1) {
-          const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
-          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + orow * D + lc * E) =
-              f32x4_t{o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv};
-        } else {
-          const int64_t slot = orow * a.num_parts + part;
-          *reinterpret_cast<f32x4_t*>(a.part_o + slot * D + lc * E) =
-              f32x4_t{o[h][0], o[h][1], o[h][2], o[h][3]};
-          if (lc == 0) {
-            a.part_ml[2 * slot] = m_h;
-            a.part_ml[2 * slot + 1] = l_h;
-          }
-        }
+        const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + orow * D + lc * E) =
+            f32x4_t{o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv};
       }
     });
   }
@@ -458,53 +497,113 @@ void decode_partition_kernel(DecodeArgs a) {
 
 // Merge of the partition states of one (sequence, query head) row:
 // M = max_p m_p, w_p = 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p l_p.
+// Four waves share a row: wave w takes partitions w, w + 4, ... (four of
+// them in flight per step), lane i owns D / 64 output elements; the four
+// partial sums are added in a fixed order through LDS, so the result does
+// not depend on timing.
+constexpr int kMergeWaves = 4;
+
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_reduce_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
+  constexpr int kUnroll = 4;
+  __shared__ float s_max[kMergeWaves];
+  __shared__ float s_acc[kMergeWaves][D + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int orow = blockIdx.x;
   const int s = orow / a.q_heads;
   const int L = clamp_len(a, s, BS);
   const int P = (L + a.part_tokens - 1) / a.part_tokens;
-  const float* ml = a.part_ml + (int64_t)orow * a.num_parts * 2;
-  const float* po = a.part_o + (int64_t)orow * a.num_parts * D + lane * PER;
+  // Partition p of row (s, h) sits at workspace row (s * num_parts + p) * q_heads + h.
+  const int h = orow - s * a.q_heads;
+  const int64_t stride = a.q_heads;                 // rows between partitions
+  const float* ml = a.part_ml + ((int64_t)s * a.num_parts * a.q_heads + h) * 2;
+  // bf16 caches keep o / l in bf16 (the weight of partition p is then
+  // w_p * l_p); f32 caches keep o unnormalised in fp32.
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const int64_t o_off = ((int64_t)s * a.num_parts * a.q_heads + h) * D + lane * PER;
+  const float* po32 = reinterpret_cast<const float*>(a.part_o) + o_off;
+  const uint16_t* po16 = reinterpret_cast<const uint16_t*>(a.part_o) + o_off;
+
   float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int p = threadIdx.x; p < P; p += 64 * kMergeWaves) M = fmaxf(M, ml[2 * p * stride]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) s_max[wave] = M;
+  __syncthreads();
+  M = s_max[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, s_max[w]);
+
   float lsum = 0.f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int p = 0; p < P; ++p) {
-    // A partition with no tokens (m = -inf) carries no weight.
-    const float w = ml[2 * p] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[2 * p] - M);
-    lsum = fmaf(w, ml[2 * p + 1], lsum);
+  for (int p0 = wave; p0 < P; p0 += kMergeWaves * kUnroll) {
+    float mv[kUnroll], lv[kUnroll], ov[kUnroll][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[(int64_t)p * D + e], acc[e]);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = min(p0 + u * kMergeWaves, P - 1);
+      mv[u] = ml[2 * p * stride];
+      lv[u] = ml[2 * p * stride + 1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        ov[u][e] = kBf16 ? __uint_as_float((uint32_t)po16[(int64_t)p * stride * D + e] << 16)
+                         : po32[(int64_t)p * stride * D + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      // A partition with no tokens (m = -inf), or past the row's last one,
+      // carries no weight.
+      const bool live = p0 + u * kMergeWaves < P && mv[u] != -INFINITY;
+      const float w = live ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f;
+      const float wl = w * lv[u];
+      lsum += wl;
+      const float wo = kBf16 ? wl : w;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wo, ov[u][e], acc[e]);
+    }
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) s_acc[wave][lane * PER + e] = acc[e];
+  if (lane == 0) s_acc[wave][D] = lsum;
+  __syncthreads();
+  if (wave != 0) return;
+  float tot[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) tot[e] = s_acc[0][lane * PER + e];
+  float ltot = s_acc[0][D];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) tot[e] += s_acc[w][lane * PER + e];
+    ltot += s_acc[w][D];
+  }
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if constexpr (sizeof(T) == 2) {
     static_assert(PER == 2, "bf16 merge writes two elements per lane");
     __bf16* out = reinterpret_cast<__bf16*>(a.out) + (int64_t)orow * D + lane * PER;
-    out[0] = (__bf16)(acc[0] * inv);
-    out[1] = (__bf16)(acc[1] * inv);
+    out[0] = (__bf16)(tot[0] * inv);
+    out[1] = (__bf16)(tot[1] * inv);
   } else {
     float* out = reinterpret_cast<float*>(a.out) + (int64_t)orow * D + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = acc[e] * inv;
+    for (int e = 0; e < PER; ++e) out[e] = tot[e] * inv;
   }
 }
 
 template <typename T, int D, int BS, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int groups = a.kv_heads / a.heads_per_wg;
-  const int64_t units = (int64_t)a.num_seqs * a.num_parts * groups;
+  const int64_t units = (int64_t)a.num_seqs * a.num_chunks * groups;
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, G>), dim3((unsigned)units),
                      dim3(64 * a.heads_per_wg), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_parts == 1) return err;
   hipLaunchKernelGGL((decode_reduce_kernel<T, D, BS>), dim3((unsigned)(a.num_seqs * a.q_heads)),
-                     dim3(64), 0, stream, a);
+                     dim3(64 * kMergeWaves), 0, stream, a);
   return hipGetLastError();
 }
 

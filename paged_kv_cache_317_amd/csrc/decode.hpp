@@ -17,8 +17,8 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* part_ml;          // [S, Hq, P, 2] (running max in log2 units, sum); split only
-  float* part_o;           // [S, Hq, P, D] unnormalised; split only
+  float* part_ml;          // [S, P, Hq, 2] (running max in log2 units, sum); split only
+  void* part_o;            // [S, P, Hq, D]: bf16 caches o / l in bf16, f32 caches o in fp32
   int64_t num_blocks;
   int32_t table_width;
   int32_t num_seqs;
@@ -27,6 +27,8 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t part_tokens;     // multiple of the block size
   int32_t num_parts;       // partitions per sequence (1: no split)
+  int32_t parts_per_unit;  // consecutive partitions one workgroup walks
+  int32_t num_chunks;      // ceil(num_parts / parts_per_unit)
   int32_t heads_per_wg;    // kv heads per workgroup (one wave each)
   uint32_t row_bytes;      // one slot: kv_heads * head_dim * element bytes
   uint32_t tile_bytes;     // 16 slots

@@ -3,6 +3,7 @@
 // invalid call launches nothing and touches no device state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -19,6 +20,12 @@
 namespace pkv {
 const char* last_error();
 }
+
+// Waves a split decode keeps when its workgroups walk several partitions
+// each (0: one partition per workgroup).
+#ifndef PKV_DECODE_WALK_WAVES
+#define PKV_DECODE_WALK_WAVES 0
+#endif
 
 // Kv heads (one wave each) per decode workgroup, when kv_heads allows it.
 #ifndef PKV_DECODE_HEADS_PER_WG
@@ -125,7 +132,9 @@ pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_head
   plan->workspace = 0;
   if (plan->num_parts > 1) {
     const int64_t rows = (int64_t)num_seqs * q_heads * plan->num_parts;
-    plan->workspace = (size_t)((round_up(2 * rows, 4) + rows * c->head_dim) * sizeof(float));
+    // (max, sum) in fp32, then o in the cache's precision (bf16: normalised).
+    plan->workspace = (size_t)(round_up(2 * rows, 4) * sizeof(float) +
+                               rows * c->head_dim * elem_bytes(c->dtype));
   }
   return PKV_OK;
 }
@@ -214,7 +223,19 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
       (int64_t)cache->block_size * cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype);
   if (block_bytes > UINT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "a block of %lld bytes exceeds 4 GiB", (long long)block_bytes);
-  const int64_t units = (int64_t)num_seqs * plan.num_parts * (cache->kv_heads / heads_per_wg);
+  // A split workgroup walks parts_per_unit consecutive partitions (emitting
+  // each partition's state), as many as keep the grid at the wave target
+  // and the walked table slice within LDS: short partitions then cost no
+  // pipeline restart each.
+  int64_t parts_per_unit = 1;
+  if (plan.num_parts > 1 && PKV_DECODE_WALK_WAVES > 0) {
+    const int64_t lds_cap = (int64_t)pkv::kMaxPartBlocks * cache->block_size / plan.part_tokens;
+    const int64_t fill =
+        (int64_t)num_seqs * cache->kv_heads * plan.num_parts / PKV_DECODE_WALK_WAVES;
+    parts_per_unit = std::max<int64_t>(1, std::min({lds_cap, fill, plan.num_parts}));
+  }
+  const int64_t num_chunks = (plan.num_parts + parts_per_unit - 1) / parts_per_unit;
+  const int64_t units = (int64_t)num_seqs * num_chunks * (cache->kv_heads / heads_per_wg);
   if (units > INT32_MAX || (int64_t)num_seqs * q_heads > INT32_MAX)
     return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)units);
 
@@ -240,6 +261,8 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
   a.max_seq_len = max_seq_len;
   a.part_tokens = (int32_t)plan.part_tokens;
   a.num_parts = (int32_t)plan.num_parts;
+  a.parts_per_unit = (int32_t)parts_per_unit;
+  a.num_chunks = (int32_t)num_chunks;
   a.heads_per_wg = heads_per_wg;
   a.row_bytes = (uint32_t)((int64_t)cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype));
   a.tile_bytes = 16u * a.row_bytes;

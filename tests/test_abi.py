@@ -114,7 +114,9 @@ def test_partition_choice(S, Hkv, max_len, req, expect):
     ws = lib().pkv_decode_workspace_size(ctypes.byref(d), S, Hkv * 4, max_len, req)
     P = -(-max_len // got)
     rows = S * Hkv * 4 * P
-    assert ws == (0 if P == 1 else (-(-2 * rows // 4) * 4 + rows * 128) * 4)
+    # fp32 (max, sum) pairs, padded to 16 bytes, then o per row in the cache
+    # precision (bf16 here: 2 bytes per element)
+    assert ws == (0 if P == 1 else -(-2 * rows // 4) * 4 * 4 + rows * 128 * 2)
 
 
 def test_partition_request_rounds_to_block_size():

@@ -237,3 +237,33 @@ def test_workspace_errors():
                               d["seq_lens"], w.cfg.scale, w.layout.max_seq_len, part_tokens=512,
                               workspace=small)
     assert e.value.status_name == "PKV_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("dtype_case", ["bf16", "f32"])
+def test_workgroups_walking_several_partitions(dtype_case):
+    """Enough short partitions that each workgroup walks several consecutive
+    ones (emitting every partition's state): the result matches the oracle.
+    A table entry outside the pool at the end of a walked span ends that
+    span there: its last partition carries an empty state, while the
+    sequence's later spans (other workgroups) still count."""
+    if dtype_case == "bf16":
+        cfg = scaled(get_config("c3_gqa4k_bf16"), num_seqs=64, len_range=(200, 512), max_len=512)
+    else:
+        cfg = scaled(get_config("c1_tiny_f32"), num_seqs=64, q_heads=16, kv_heads=8,
+                     seq_lens=(), len_range=(200, 512), max_len=512, pool_blocks=0)
+    w = generate_host(cfg)
+    # 64 sequences x 8 kv heads x 32 partitions of 16 tokens: 8 partitions per workgroup
+    log(f"walk {dtype_case}: S={cfg.num_seqs} part=16")
+    d = upload(w)
+    table = w.block_table.copy()
+    s_bad = 5
+    table[s_bad, 7] = -1                                 # positions >= 112 unreadable
+    out = _decode(d, w, part_tokens=16, block_table=to_device(table, None))
+    # Sequence s_bad attends to positions 0..111 and 128..L-1: the oracle sees
+    # that as a sequence 16 tokens shorter whose table skips logical block 7.
+    ref_table = w.block_table.copy()
+    ref_table[s_bad] = np.concatenate([w.block_table[s_bad, :7], w.block_table[s_bad, 8:], [-1]])
+    lens = w.seq_lens.copy()
+    lens[s_bad] -= cfg.block_size
+    ref = oracle_decode(w, seq_lens=lens, block_table=ref_table)
+    compare(out, ref, cfg.dtype)
