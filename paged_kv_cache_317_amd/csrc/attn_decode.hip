@@ -60,7 +60,11 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kTile = 16;
-constexpr int kMaxWavesPerWg = 4;
+// Kv heads (one wave each) a decode workgroup can hold.
+#ifndef PKV_DECODE_MAX_WAVES
+#define PKV_DECODE_MAX_WAVES 4
+#endif
+constexpr int kMaxWavesPerWg = PKV_DECODE_MAX_WAVES;
 
 template <typename T>
 struct Storage;
@@ -117,7 +121,8 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s, int block_s
 #define PKV_DECODE_WAVES_PER_EU 4
 #endif
 template <typename T, int D, int BS, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * kMaxWavesPerWg)
+__attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int E = Storage<T>::kPerVec;
