@@ -8,28 +8,37 @@
  * maps logical block j (token positions j*block_size .. j*block_size +
  * block_size - 1) to a physical block anywhere in the pool ("PagedAttention
  * Explained: Virtual Memory for the KV Cache", section "How PagedAttention
- * works", steps 1-3).  Three operations act on such a cache:
+ * works", steps 1-3).  The operations on such a cache:
  *
  *   pkv_paged_kv_write     store new tokens' K/V rows in their slots
  *   pkv_paged_attn_decode  attention of one query token per sequence,
  *                          gathering K/V through the block table (step 5)
+ *   pkv_paged_attn_extend  the same for several new tokens per sequence
+ *                          (prefill, chunked extend), causal
  *   pkv_paged_block_copy   copy whole blocks, the copy step of copy-on-write
  *                          ("Sharing blocks between sequences")
+ *   pkv_paged_block_move   copy blocks between a device pool and a pool in
+ *                          pinned host memory (swapping, "Preemption and
+ *                          scheduling")
+ * and, on the host, a block manager (pkv_bm_*) that hands out the slots,
+ * tables, copy-on-write pairs and swap pairs these operations consume.
  *
- * Conventions shared by every entry point
- * ---------------------------------------
+ * Conventions shared by every device entry point
+ * ----------------------------------------------
  * Memory.   Every buffer argument is a device pointer to memory the caller
  *           allocated (hipMalloc or a framework allocator) and keeps alive
- *           until the work on `stream` has finished.  The library never
- *           allocates, frees or synchronises; it launches kernels on
- *           `stream` (a hipStream_t passed as void*; NULL is the default
- *           stream) and returns before they run.
+ *           until the work on `stream` has finished; pkv_paged_block_move
+ *           also takes pinned host memory.  The library never allocates,
+ *           frees or synchronises; it launches kernels on `stream` (a
+ *           hipStream_t passed as void*; NULL is the default stream) and
+ *           returns before they run.
  * Layouts.  All arrays are dense and row-major.
  *           cache:  [num_blocks, block_size, kv_heads, head_dim] of `dtype`;
  *                   the row of slot `s` (token offset s % block_size of
  *                   physical block s / block_size) starts at element
  *                   s * kv_heads * head_dim.
- *           q, out: [num_seqs, q_heads, head_dim] of the cache dtype.
+ *           q, out: [num_seqs, q_heads, head_dim] of the cache dtype for
+ *                   decode; [num_tokens, q_heads, head_dim] for extend.
  *           bf16 is IEEE binary32's upper 16 bits (bfloat16).
  *           Cache, q, k, v and out pointers must be 16-byte aligned.
  * Errors.   Arguments are checked on the host before anything is launched;
@@ -40,10 +49,10 @@
  * Device-side safety.  Values read from device memory (slots, table entries,
  *           copy pairs) cannot be checked on the host.  Kernels never touch
  *           memory outside the pool for an id outside it: such a slot or copy
- *           pair is skipped, and decode stops reading a sequence's partition
- *           at such a table entry (the output for that sequence is then
- *           unspecified).  That is a guard, not a contract: callers must
- *           pass valid ids.
+ *           pair is skipped, decode stops reading a sequence's partition at
+ *           such a table entry (the output for that sequence is then
+ *           unspecified) and extend stops the sequence there.  That is a
+ *           guard, not a contract: callers must pass valid ids.
  * Threads.  The library keeps no state between calls apart from the
  *           thread-local last-error message, so calls from several host
  *           threads are safe; ordering between them is the streams'.
@@ -130,7 +139,10 @@ pkv_status pkv_paged_kv_write(const void* k, const void* v,
  *   workspace    device scratch of at least pkv_decode_workspace_size()
  *                bytes when the call splits (more than one partition);
  *                may be NULL when that size is 0.  Contents need no
- *                initialisation and are left undefined.
+ *                initialisation and are left undefined.  It holds each
+ *                partition's max and sum (fp32) and output (bf16 caches:
+ *                normalised, in bf16; f32 caches: fp32), merged by a second
+ *                kernel in a fixed order.
  * Supported: f32 with head_dim 64, bf16 with head_dim 128; block_size 16 or
  * 32; G in {1, 2, 4, 8}.
  */
@@ -333,7 +345,8 @@ pkv_status pkv_bm_preempt(pkv_block_manager* bm, int64_t seq);
  * brings it back into fresh device blocks and writes the (host, device)
  * pairs.  A swapped sequence cannot grow or be forked; sharing and prefix
  * registration do not survive a swap.  Both fail with PKV_ERR_NO_BLOCKS,
- * changing nothing, when the target pool is short. */
+ * changing nothing, when the target pool is short, and with PKV_ERR_SHAPE
+ * when cap is below the sequence's block count. */
 pkv_status pkv_bm_set_swap_space(pkv_block_manager* bm, int32_t host_blocks);
 pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq, int64_t* pairs,
                            int32_t cap, int32_t* n);
@@ -373,7 +386,8 @@ pkv_status pkv_capacity(int64_t num_blocks, int32_t block_size,
  * host memory is reached through its device mapping, and pageable host
  * memory is refused with PKV_ERR_UNSUPPORTED (no launch).  Pairs naming a
  * block outside its pool are skipped.  Within one call the destination ids
- * must be distinct.
+ * must be distinct, and when source and destination are the same pool no
+ * destination may also be a source (as for pkv_paged_block_copy).
  */
 pkv_status pkv_paged_block_move(const int64_t* pairs, int32_t num_pairs,
                                 const void* src_k, const void* src_v,

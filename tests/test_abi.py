@@ -122,3 +122,53 @@ def test_partition_choice(S, Hkv, max_len, req, expect):
 def test_partition_request_rounds_to_block_size():
     d = _desc(bs=32)
     assert lib().pkv_decode_partition_tokens(ctypes.byref(d), 4, 32, 10_000, 100) == 128
+
+
+def _extend(desc, S=2, T=40, Hq=32, maxq=20, scale=0.1, q=1 << 12, kc=1 << 12, vc=1 << 12,
+            table=1 << 12, lens=1 << 12, qs=1 << 12, out=1 << 12, width=8):
+    return lib().pkv_paged_attn_extend(q, kc, vc, ctypes.byref(desc) if desc else None, table,
+                                       width, lens, qs, S, T, Hq, maxq, scale, out, None)
+
+
+def test_extend_argument_checks_run_before_any_launch():
+    assert _status(_extend(None)) == "NULL"
+    assert _status(_extend(_desc(dtype=9))) == "DTYPE"
+    assert _status(_extend(_desc(), Hq=30)) == "SHAPE"
+    assert _status(_extend(_desc(dtype=0))) == "UNSUPPORTED"         # f32: no extend kernel
+    assert _status(_extend(_desc(d=64))) == "UNSUPPORTED"
+    assert _status(_extend(_desc(bs=8))) == "UNSUPPORTED"
+    assert _status(_extend(_desc(), Hq=8 * 16)) == "UNSUPPORTED"     # group 16 not built
+    assert _status(_extend(_desc(), scale=0.0)) == "SHAPE"
+    assert _status(_extend(_desc(), scale=-1.0)) == "SHAPE"
+    assert _status(_extend(_desc(), scale=float("nan"))) == "SHAPE"
+    assert _status(_extend(_desc(), scale=float("inf"))) == "SHAPE"
+    assert _status(_extend(_desc(), S=-1)) == "SHAPE"
+    assert _status(_extend(_desc(), T=-1)) == "SHAPE"
+    assert _status(_extend(_desc(), maxq=-1)) == "SHAPE"
+    assert _status(_extend(_desc(), qs=0)) == "NULL"
+    assert _status(_extend(_desc(), out=(1 << 12) + 4)) == "ALIGN"
+    assert _status(_extend(_desc(), width=0)) == "SHAPE"
+    # nothing to compute: OK with NULL pointers
+    for kw in (dict(S=0), dict(T=0), dict(maxq=0)):
+        assert _status(_extend(_desc(), q=0, kc=0, vc=0, table=0, lens=0, qs=0, out=0,
+                               **kw)) == "OK"
+
+
+def test_block_move_argument_checks_run_before_any_launch():
+    L = lib()
+    a, b = _desc(nb=64), _desc(nb=16)
+    mv = L.pkv_paged_block_move
+    assert _status(mv(1 << 12, 2, 1 << 12, 1 << 12, None, 1 << 12, 1 << 12, ctypes.byref(b),
+                      None)) == "NULL"
+    assert _status(mv(1 << 12, 2, 1 << 12, 1 << 12, ctypes.byref(a), 1 << 12, 1 << 12,
+                      ctypes.byref(_desc(nb=16, bs=32)), None)) == "SHAPE"   # block shapes differ
+    assert _status(mv(1 << 12, 2, 1 << 12, 1 << 12, ctypes.byref(a), 1 << 12, 1 << 12,
+                      ctypes.byref(_desc(nb=16, dtype=0)), None)) == "SHAPE"
+    assert _status(mv(1 << 12, -1, 1 << 12, 1 << 12, ctypes.byref(a), 1 << 12, 1 << 12,
+                      ctypes.byref(b), None)) == "SHAPE"
+    assert _status(mv(None, 2, 1 << 12, 1 << 12, ctypes.byref(a), 1 << 12, 1 << 12,
+                      ctypes.byref(b), None)) == "NULL"
+    assert _status(mv(1 << 12, 2, (1 << 12) + 4, 1 << 12, ctypes.byref(a), 1 << 12, 1 << 12,
+                      ctypes.byref(b), None)) == "ALIGN"
+    assert _status(mv(None, 0, None, None, ctypes.byref(a), None, None, ctypes.byref(b),
+                      None)) == "OK"
