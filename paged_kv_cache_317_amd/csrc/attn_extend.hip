@@ -82,6 +82,10 @@ static_assert(kKeys % kStep == 0, "whole rows per thread");
 #define PKV_EXTEND_PINGPONG 0
 #endif
 static_assert(!PKV_EXTEND_PINGPONG || kWaves == 8, "ping-pong needs two waves per SIMD");
+// K/V tiles in flight in registers while one computes (1 or 2).
+#ifndef PKV_EXTEND_DEPTH
+#define PKV_EXTEND_DEPTH 2
+#endif
 constexpr int kBufs = PKV_EXTEND_PINGPONG ? 3 : 2;
 
 // Unit order: 0 = the units of one XCD contiguous, 1 = query tiles from the
@@ -429,6 +433,40 @@ void extend_kernel(ExtendArgs a) {
         softmax(j);
       }
       __syncthreads();
+    }
+#elif PKV_EXTEND_DEPTH == 2
+    // Two register sets: while tile t computes, tiles t+1 and t+2 are in
+    // flight; tile t+1 is written to LDS after tile t and its registers are
+    // refilled with tile t+3.
+    u32x4_t kr2[kRowsPerThread], vr2[kRowsPerThread];
+    if (ntiles > 1) {
+      load_tile(ent, kr, vr);                  // tile 1 -> set A
+      fetch_entries(2, ent);
+    }
+    if (ntiles > 2) {
+      load_tile(ent, kr2, vr2);                // tile 2 -> set B
+      fetch_entries(3, ent);
+    }
+    __syncthreads();
+    auto step = [&](int t, u32x4_t (&ka_)[kRowsPerThread], u32x4_t (&va_)[kRowsPerThread]) {
+      if (tile_active(t)) {
+        qk(t & 1);
+        softmax(t);
+        pv(t & 1);
+      }
+      if (t + 1 < ntiles) {
+        store_tile(t + 1, (t + 1) & 1, ka_, va_);
+        if (t + 3 < ntiles) {
+          load_tile(ent, ka_, va_);
+          fetch_entries(t + 4, ent);
+        }
+      }
+      __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, kr, vr);                         // stores tile t+1 (set A)
+      if (t + 1 >= ntiles) break;
+      step(t + 1, kr2, vr2);                   // stores tile t+2 (set B)
     }
 #else
     __syncthreads();

@@ -1,0 +1,93 @@
+"""Seeded random shapes across the supported space, decode and extend, each
+compared with the fp64 oracle on every output row: lengths on and off block
+and tile boundaries, every built G and block size, explicit partition
+lengths, sequences of length 0 or 1, random table placement and pool slack."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_317_amd as pkv
+from workloads.generate import f32_to_bf16_bits
+
+from helpers import compare, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _pool(rng, lens, BS, Hkv, D, dtype, slack):
+    """A pool with each sequence's blocks at random places (the test's own
+    layout, built without the workload generator)."""
+    nblk = [-(-int(L) // BS) for L in lens]
+    NB = sum(nblk) + slack
+    perm = rng.permutation(NB)
+    MB = max(max(nblk), 1) + int(rng.integers(0, 3))
+    table = np.full((len(lens), MB), -1, dtype=np.int32)
+    cur = 0
+    for s, n in enumerate(nblk):
+        table[s, :n] = perm[cur:cur + n]
+        cur += n
+    shape = (NB, BS, Hkv, D)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    y = rng.standard_normal(shape, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x), f32_to_bf16_bits(y), table
+    return x, y, table
+
+
+def _values(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_shapes(seed):
+    rng = np.random.default_rng(5000 + seed)
+    dtype = "f32" if seed % 4 == 0 else "bf16"
+    D = 64 if dtype == "f32" else 128
+    BS = int(rng.choice([16, 32]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.integers(1, 40))
+    lens = rng.integers(0, 1200, size=S)
+    lens[rng.integers(0, S)] = int(rng.choice([0, 1, BS, BS + 1, 16 * 7, 16 * 7 + 3]))
+    part = int(rng.choice([0, 0, 16, 64, 256, 512]))
+    kc, vc, table = _pool(rng, lens, BS, Hkv, D, dtype, int(rng.integers(0, 20)))
+    q = _values(rng, (S, Hkv * G, D), dtype)
+    scale = float(rng.uniform(0.02, 0.2))
+    log(f"decode seed {seed}: {dtype} S={S} BS={BS} Hkv={Hkv} G={G} part={part}")
+    max_len = int(lens.max())
+    out = pkv.paged_attn_decode(to_device(q, dtype), to_device(kc, dtype), to_device(vc, dtype),
+                                to_device(table, None), to_device(lens.astype(np.int32), None),
+                                scale, max_len, part_tokens=part)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(q, kc, vc, table, lens, scale, dtype)
+    compare(out, ref, dtype)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_extend_random_shapes(seed):
+    rng = np.random.default_rng(6000 + seed)
+    BS = int(rng.choice([16, 32]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.integers(1, 8))
+    ctx = rng.integers(0, 700, size=S)
+    new = rng.integers(0, 300, size=S)
+    new[rng.integers(0, S)] = int(rng.choice([0, 1, 63, 64, 65, 256 // G]))
+    lens = ctx + new
+    kc, vc, table = _pool(rng, lens, BS, Hkv, 128, "bf16", int(rng.integers(0, 20)))
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    T = int(qs[-1])
+    q = _values(rng, (max(T, 1), Hkv * G, 128), "bf16")[:T]
+    scale = float(rng.uniform(0.02, 0.2))
+    log(f"extend seed {seed}: S={S} T={T} BS={BS} Hkv={Hkv} G={G}")
+    if T == 0:
+        pytest.skip("no new tokens drawn")
+    out = pkv.paged_attn_extend(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
+                                to_device(table, None), to_device(lens.astype(np.int32), None),
+                                to_device(qs, None), scale, int(new.max()))
+    torch.cuda.synchronize()
+    ref = oracle.extend_attention(q, kc, vc, table, lens, qs, scale, "bf16")
+    compare(out, ref, "bf16")
