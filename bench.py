@@ -285,6 +285,45 @@ def allocator_report(cfg, lay):
         "max_sequences_contiguous": lay.num_blocks * BS // cfg.max_len,
         "append_ns_per_token": round(t_bulk / max(tokens, 1) * 1e9, 2),
         "decode_append_us": round(t_step / S * 1e6, 3),
+        "prefix_cache": prefix_cache_report(cfg, lay),
+    }
+
+
+def prefix_cache_report(cfg, lay):
+    """The batch's requests as token ids: a common system prompt (the batch's
+    shared prefix, else 1024 tokens) then private tokens up to each length,
+    started through the prefix cache of the native block manager (a lookup
+    over the full blocks, then the rest stored with their token ids)."""
+    import numpy as np
+    from paged_kv_cache_317_amd.block_manager import BlockManager
+    BS, S = cfg.block_size, cfg.num_seqs
+    lens = lay.seq_lens.astype(np.int64)
+    rng = np.random.default_rng(cfg.seed)
+    common = int(cfg.prefix_tokens or min(1024, int(lens.min())))
+    system = rng.integers(0, 32000, size=common).astype(np.int32)
+    reqs = [np.concatenate([system, rng.integers(0, 32000, size=max(int(L) - common, 0))
+                            .astype(np.int32)])[:int(L)] for L in lens]
+    bm = BlockManager(lay.num_blocks, BS)
+    t_lookup = t_store = 0.0
+    reused = 0
+    for i, toks in enumerate(reqs):
+        t0 = time.perf_counter()
+        n = bm.add_cached(i, toks)
+        t1 = time.perf_counter()
+        bm.append_tokens(i, toks[n:])
+        t_store += time.perf_counter() - t1
+        t_lookup += t1 - t0
+        reused += n
+    st = bm.stats()
+    stored = int(lens.sum()) - reused
+    return {
+        "requests": S,
+        "common_prefix_tokens": common,
+        "reused_tokens": reused,
+        "allocated_blocks": st["allocated_blocks"],
+        "blocks_without_reuse": int(sum(-(-int(L) // BS) for L in lens)),
+        "add_cached_us_per_request": round(t_lookup / S * 1e6, 2),
+        "append_tokens_ns_per_token": round(t_store / max(stored, 1) * 1e9, 2),
     }
 
 
