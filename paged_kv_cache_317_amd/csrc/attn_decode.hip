@@ -43,9 +43,14 @@
 // a sequence needs is read from HBM exactly once per call.
 //
 // Split-K (long contexts): with more than one partition per sequence each
-// wave writes its unnormalised state (max, sum, o[D]) per head to the
-// workspace and a second kernel merges the partitions with the log-sum-exp
-// rule in a fixed order (deterministic, no atomics).
+// wave emits its partition's state per head -- running max and sum in fp32,
+// the output normalised by the sum and rounded to bf16 for bf16 caches
+// (unnormalised fp32 for f32 caches) -- into the workspace, ordered
+// [sequence, partition, head] so that a wave's heads are adjacent and leave
+// through its LDS tile in whole runs.  A second kernel merges the
+// partitions with the log-sum-exp rule in a fixed order (deterministic, no
+// atomics).  A workgroup may walk several consecutive partitions (a build
+// option), emitting each one's state at its last tile.
 #include <utility>
 
 #include "device_common.hpp"
