@@ -170,3 +170,45 @@ def test_extend_full_size_sampled(name, nsample):
     rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
     mabs, mrel = compare(out, ref, "bf16", rows=rows)
     log(f"  sequences {seqs}: max-abs {mabs:.3e} row max-rel {mrel:.3e}")
+
+
+def test_extend_and_block_move_replay_inside_a_captured_graph():
+    """Slot write, extend and a device-to-pinned-host block move captured in
+    one HIP graph, replayed several times with eager work in between; every
+    replay matches the eager result bit for bit."""
+    cfg = EXTEND_CONFIGS["x5_extend_mha_bf16"]
+    w = generate_extend_host(cfg)
+    d = _upload(w)
+    out = torch.empty_like(d["q"])
+    NB = w.layout.num_blocks
+    host_k = torch.zeros((8,) + tuple(d["k_cache"].shape[1:]), dtype=torch.bfloat16).pin_memory()
+    host_v = torch.zeros_like(host_k).pin_memory()
+    pairs = torch.tensor([[b, i] for i, b in enumerate(range(0, NB, max(NB // 8, 1)))][:8],
+                         dtype=torch.int64, device="cuda")
+
+    def step():
+        pkv.paged_kv_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+        pkv.paged_attn_extend(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                              d["seq_lens"], d["query_start"], cfg.scale, w.max_query_len,
+                              out=out)
+        pkv.paged_block_move(pairs, d["k_cache"], d["v_cache"], host_k, host_v)
+
+    step()
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    eager_hk, eager_hv = host_k.clone(), host_v.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        host_k.zero_()
+        host_v.zero_()
+        d["k_cache"].copy_(to_device(w.k_cache, "bf16"))
+        d["v_cache"].copy_(to_device(w.v_cache, "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager_out.view(torch.int16)), f"replay {r}"
+        assert torch.equal(host_k.view(torch.int16), eager_hk.view(torch.int16)), f"replay {r}"
+        assert torch.equal(host_v.view(torch.int16), eager_hv.view(torch.int16)), f"replay {r}"
