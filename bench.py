@@ -17,9 +17,9 @@ same batch.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
-With a prefill/extend workload (``--workload x2_prefill_bf16`` or
-``x3_extend_bf16``) the step is the slot write of every new token followed by
-``paged_attn_extend``, and ``value`` is the causal attention's TFLOP/s
+With a prefill/extend workload (``--workload x2_prefill_bf16``,
+``x3_extend_bf16`` or ``x6_long_extend_bf16``) the step is the slot write of
+every new token followed by ``paged_attn_extend``, and ``value`` is the causal attention's TFLOP/s
 against the bf16 matrix-core peak.
 """
 
@@ -366,15 +366,23 @@ def extend_bench(args):
           file=sys.stderr, flush=True)
     w = generate_extend_device(cfg, device=dev)
     lay = w.layout
-    maxq = w.max_query_len
+    maxq, maxl = w.max_query_len, w.max_seq_len
     out = torch.empty_like(w.q)
+    T = w.num_tokens
+    part = pkv.extend_partition_tokens(w.k_cache, cfg.num_seqs, T, cfg.q_heads, maxq, maxl,
+                                       args.part_tokens or 0)
+    ws_bytes = pkv.extend_workspace_size(w.k_cache, cfg.num_seqs, T, cfg.q_heads, maxq, maxl,
+                                         args.part_tokens or 0)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    num_parts = -(-maxl // part)
 
     def write():
         pkv.paged_kv_write(w.new_k, w.new_v, w.slot_mapping, w.k_cache, w.v_cache)
 
     def attend():
         pkv.paged_attn_extend(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens,
-                              w.query_start_dev, cfg.scale, maxq, out=out)
+                              w.query_start_dev, cfg.scale, maxq, maxl, out=out,
+                              part_tokens=args.part_tokens or 0, workspace=workspace)
 
     for _ in range(args.warmup):
         write()
@@ -396,7 +404,6 @@ def extend_bench(args):
     print(f"# {K} steps: {step_ms:.4f} ms/step, extend {attn_ms:.4f} ms", file=sys.stderr,
           flush=True)
     flops, _ = causal_work(lay.seq_lens, w.query_start, cfg.q_heads, cfg.head_dim)
-    T = w.num_tokens
     row = cfg.kv_heads * cfg.head_dim * cfg.elem_bytes
     kv_bytes = int(lay.seq_lens.astype(np.int64).sum()) * row * 2
     io_bytes = 2 * T * cfg.q_heads * cfg.head_dim * cfg.elem_bytes
@@ -450,6 +457,8 @@ def extend_bench(args):
             "new_tokens": T,
             "seq_lens": [int(lay.seq_lens.min()), int(lay.seq_lens.max())],
             "pool_blocks": lay.num_blocks,
+            "partition_tokens": part,
+            "partitions": num_parts,
             "step": "paged_kv_write (every new token) + paged_attn_extend",
         },
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),

@@ -181,9 +181,23 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,
  *                written whatever it holds
  *   max_query_len host-side bound on every n (sizes the grid); query rows
  *                j >= max_query_len of a sequence are not written
+ *   max_seq_len  host-side bound on every seq_lens[s] (sizes the split);
+ *                a sequence is cut to min(seq_lens[s], max_seq_len,
+ *                table_width * block_size) keys
  *   scale        softmax scale, positive and finite (PKV_ERR_SHAPE otherwise)
- * No workspace.  Supported: bf16 caches with head_dim 128, block_size 16 or
- * 32, G in {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.
+ *   part_tokens  split-K partition length in keys (rounded up to a multiple
+ *                of 64), or 0 to let the library choose: it splits only when
+ *                the batch has too few (sequence, kv head, query tile) units
+ *                to fill the device and the keys are long;
+ *                pkv_extend_partition_tokens() reports the choice
+ *   workspace    device scratch of at least pkv_extend_workspace_size()
+ *                bytes when the call splits; may be NULL when that size is
+ *                0.  Contents need no initialisation and are left undefined.
+ *                It holds each partition's max and sum (fp32) and normalised
+ *                output (bf16) per query row and head, merged by a second
+ *                kernel in a fixed order.
+ * Supported: bf16 caches with head_dim 128, block_size 16 or 32, G in
+ * {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.
  */
 pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache,
                                  const void* v_cache,
@@ -192,8 +206,29 @@ pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache,
                                  int32_t table_width, const int32_t* seq_lens,
                                  const int32_t* query_start, int32_t num_seqs,
                                  int32_t num_tokens, int32_t q_heads,
-                                 int32_t max_query_len, float scale, void* out,
+                                 int32_t max_query_len, int32_t max_seq_len,
+                                 float scale, void* out, int32_t part_tokens,
+                                 void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * Partition length (keys) pkv_paged_attn_extend uses for these arguments;
+ * the call is split when it is below max_seq_len.  Returns 0 on invalid
+ * arguments (see pkv_last_error()).
+ */
+int32_t pkv_extend_partition_tokens(const pkv_cache_desc* cache,
+                                    int32_t num_seqs, int32_t num_tokens,
+                                    int32_t q_heads, int32_t max_query_len,
+                                    int32_t max_seq_len, int32_t part_tokens);
+
+/*
+ * Workspace bytes pkv_paged_attn_extend needs for these arguments (0 when it
+ * does not split).  Returns 0 on invalid arguments as well.
+ */
+size_t pkv_extend_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
+                                 int32_t num_tokens, int32_t q_heads,
+                                 int32_t max_query_len, int32_t max_seq_len,
+                                 int32_t part_tokens);
 
 /*
  * Partition length (tokens) pkv_paged_attn_decode uses for these arguments;

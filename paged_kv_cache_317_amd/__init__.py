@@ -1,4 +1,4 @@
-"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+"""Paged KV-cache attention (decode and extend) for AMD Instinct MI355X (gfx950).
 
 The kernels and the C ABI live in ``libpkv.so`` (sources in ``csrc/``, header
 ``include/pkv.h`` at the repository root); ``ops`` wraps them for torch
@@ -11,6 +11,8 @@ from .ops import (
     cache_desc,
     decode_partition_tokens,
     decode_workspace_size,
+    extend_partition_tokens,
+    extend_workspace_size,
     paged_attn_decode,
     paged_attn_extend,
     paged_block_copy,
@@ -25,6 +27,8 @@ __all__ = [
     "cache_desc",
     "decode_partition_tokens",
     "decode_workspace_size",
+    "extend_partition_tokens",
+    "extend_workspace_size",
     "paged_attn_decode",
     "paged_attn_extend",
     "paged_block_copy",

@@ -53,7 +53,9 @@ SIGNATURES = {
     "pkv_paged_attn_decode": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32,
                                      _f32, _vp, _i32, _vp, _sz, _vp]),
     "pkv_paged_attn_extend": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _vp, _i32, _i32,
-                                     _i32, _i32, _f32, _vp, _vp]),
+                                     _i32, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _vp]),
+    "pkv_extend_partition_tokens": (_i32, [_desc, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_extend_workspace_size": (_sz, [_desc, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_partition_tokens": (_i32, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_decode_workspace_size": (_sz, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_paged_block_copy": (_i32, [_vp, _i32, _vp, _vp, _desc, _vp]),

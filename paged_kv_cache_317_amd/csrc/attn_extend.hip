@@ -16,11 +16,16 @@
 // Work decomposition
 //   column    one (query token, query head) pair of one kv head; the G heads
 //             of a token are adjacent columns
-//   workgroup 128 columns (128 / G tokens) of one sequence and kv head;
-//             four waves of 32 columns (two 16-column MFMA groups each;
-//             the group count is a build option)
+//   workgroup 256 columns (256 / G tokens) of one sequence and kv head;
+//             eight waves of 32 columns (two 16-column MFMA groups each;
+//             wave and group counts are build options)
 //   tile      64 consecutive key positions, staged in LDS once per
-//             workgroup and read by all four waves
+//             workgroup and read by all eight waves
+//   partition a split call (num_parts > 1) also cuts the keys into
+//             part_tokens-long ranges, one workgroup per range; each writes
+//             its running max, sum and normalised output per column, and a
+//             second kernel merges them in a fixed order (the same
+//             max-rescaled combination the online softmax applies per tile)
 // Workgroups are ordered so that the query tiles of one (sequence, kv head)
 // land on one XCD (workgroup b runs on XCD b mod 8) and share its L2.
 //
@@ -55,7 +60,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kD = 128;                  // head_dim
-constexpr int kKeys = 64;                // key positions per tile
+constexpr int kKeys = kExtendKeys;       // key positions per tile
 constexpr int kWaves = PKV_EXTEND_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = kThreads / 16;     // K/V rows one pass of the workgroup loads
@@ -76,40 +81,11 @@ constexpr int kVTile = kKeys * kVRow;
 static_assert(kExtendCols == kWaves * 16 * kGroups, "kWaves waves of kGroups 16-column groups");
 static_assert(kKeys % kStep == 0, "whole rows per thread");
 
-// Ping-pong schedule between the two halves of an 8-wave workgroup (three
-// LDS tile buffers), or one wave-synchronous loop (two buffers).
-#ifndef PKV_EXTEND_PINGPONG
-#define PKV_EXTEND_PINGPONG 0
-#endif
-static_assert(!PKV_EXTEND_PINGPONG || kWaves == 8, "ping-pong needs two waves per SIMD");
-// K/V tiles in flight in registers while one computes (1 or 2).
-#ifndef PKV_EXTEND_DEPTH
-#define PKV_EXTEND_DEPTH 2
-#endif
-constexpr int kBufs = PKV_EXTEND_PINGPONG ? 3 : 2;
+constexpr int kBufs = 2;   // LDS tile buffers
 
-// Unit order: 0 = the units of one XCD contiguous, 1 = query tiles from the
-// last down, kv head fastest (the kv heads of a tile spread over the XCDs,
-// one kv head's tiles stay on one XCD when kv_heads is a multiple of 8).
-#ifndef PKV_EXTEND_ORDER
-#define PKV_EXTEND_ORDER 2
-#endif
 #ifndef PKV_EXTEND_WAVES_PER_EU
 #define PKV_EXTEND_WAVES_PER_EU 2
 #endif
-
-// Optional wave priority: raised while a wave issues its matrix products,
-// so that the scheduler keeps the matrix pipe fed from whichever wave is in
-// that phase.
-#ifndef PKV_EXTEND_PRIO
-#define PKV_EXTEND_PRIO 0
-#endif
-__device__ __forceinline__ void mfma_phase(bool on) {
-  if (PKV_EXTEND_PRIO) {
-    if (on) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-  }
-}
 
 __device__ __forceinline__ bf16x8_t cat(bf16x4_t lo, bf16x4_t hi) {
   return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -131,34 +107,22 @@ void extend_kernel(ExtendArgs a) {
   __shared__ __attribute__((aligned(16))) char s_v[kBufs][kVTile];
   __shared__ int s_first_bad;
 
-#if PKV_EXTEND_ORDER == 0
-  const int per_xcd = (a.units + 7) / 8;
-  const int unit = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (unit >= a.units) return;
-  const int qt = a.q_tiles - 1 - unit % a.q_tiles;   // later (longer) query tiles first
-  const int rest = unit / a.q_tiles;
-  const int g = rest % a.kv_heads;
-  const int s = rest / a.kv_heads;
-#elif PKV_EXTEND_ORDER == 1
-  const int unit = (int)blockIdx.x;
-  if (unit >= a.units) return;
-  const int g = unit % a.kv_heads;
-  const int rest = unit / a.kv_heads;
-  const int s = rest % a.num_seqs;
-  const int qt = a.q_tiles - 1 - rest / a.num_seqs;  // later (longer) query tiles first
-#else
-  // (sequence, kv head) pairs go round-robin over the XCDs; on its XCD a
-  // pair's query tiles are consecutive, so they run side by side and read
-  // the pair's keys and values through the same L2.
+  // (sequence, kv head) pairs go round-robin over the XCDs (workgroup b runs
+  // on XCD b mod 8); on its XCD a pair's query tiles are consecutive, so they
+  // run side by side and read the pair's keys and values through one L2.
+  // A split call (num_parts > 1) also cuts each query tile's keys into
+  // partitions of part_tokens; the query tiles of one partition are adjacent.
   const int unit = (int)blockIdx.x;
   const int xcd = unit % 8;
   const int local = unit / 8;
-  const int pair = (local / a.q_tiles) * 8 + xcd;
-  const int qt = a.q_tiles - 1 - local % a.q_tiles;  // later (longer) query tiles first
+  const int per_pair = a.q_tiles * a.num_parts;
+  const int pair = (local / per_pair) * 8 + xcd;
+  const int li = local % per_pair;
+  const int part = li / a.q_tiles;
+  const int qt = a.q_tiles - 1 - li % a.q_tiles;     // later (longer) query tiles first
   const int g = pair % a.kv_heads;
   const int s = pair / a.kv_heads;
   if (s >= a.num_seqs) return;
-#endif
 
   const int q0 = a.query_start[s];
   const int n_raw = a.query_start[s + 1] - q0;
@@ -175,7 +139,7 @@ void extend_kernel(ExtendArgs a) {
   // Keys this workgroup may read: below every query's position + 1 and the
   // sequence length; a table entry outside the pool ends the sequence at
   // that block.
-  int kv_end = max(min(L, a.table_width * BS), 0);
+  int kv_end = max(min(min(L, a.max_seq_len), a.table_width * BS), 0);
   int kv_hi = max(min(ctx + j1, kv_end), 0);
   const int nblk = (kv_hi + BS - 1) / BS;
   const int32_t* trow = a.block_table + (int64_t)s * a.table_width;
@@ -188,8 +152,11 @@ void extend_kernel(ExtendArgs a) {
   __syncthreads();
   kv_end = min(kv_end, s_first_bad * BS);
   kv_hi = min(kv_hi, kv_end);
-  const int ntiles = (kv_hi + kKeys - 1) / kKeys;
   const int last_blk = max((kv_hi - 1) / BS, 0);
+  // This unit's tiles: keys [part * part_tokens, min(+part_tokens, kv_hi)).
+  const int t_first = part * (a.part_tokens / kKeys);
+  const int t_stop = min(t_first + a.part_tokens / kKeys, (kv_hi + kKeys - 1) / kKeys);
+  const int ntiles = max(t_stop - t_first, 0);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -295,7 +262,6 @@ void extend_kernel(ExtendArgs a) {
 
   auto qk = [&](int buf) {
     const char* kt = s_k[buf];
-    mfma_phase(true);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       u32x4_t ka[4];
@@ -313,7 +279,6 @@ void extend_kernel(ExtendArgs a) {
         sacc[cg][kb] = acc;
       }
     }
-    mfma_phase(false);
   };
 
   auto softmax = [&](int tile) {
@@ -369,7 +334,6 @@ void extend_kernel(ExtendArgs a) {
 
   auto pv = [&](int buf) {
     const char* vt = s_v[buf];
-    mfma_phase(true);
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
@@ -389,102 +353,77 @@ void extend_kernel(ExtendArgs a) {
         lsum[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             ones, cat(pb[cg][2 * kp], pb[cg][2 * kp + 1]), lsum[cg], 0, 0, 0);
     }
-    mfma_phase(false);
   };
 
   if (ntiles > 0) {
+    // Two register sets: while tile t computes, tiles t+1 and t+2 are in
+    // flight; tile t+1 is written to LDS after tile t, one barrier per tile.
+    // Local tile i is absolute tile t_first + i, in LDS buffer i & 1.
     int ent[kRowsPerThread];
     u32x4_t kr[kRowsPerThread], vr[kRowsPerThread];
-    fetch_entries(0, ent);
-    load_tile(ent, kr, vr);
-    fetch_entries(1, ent);
-    store_tile(0, 0, kr, vr);
-#if PKV_EXTEND_PINGPONG
-    // Two halves of the workgroup (waves 0-3 and 4-7, one of each per SIMD)
-    // run half a tile apart.  Phase p ends with a barrier; in it one half
-    // issues matrix products (PV of tile j-1 and QK of tile j) while the
-    // other computes the softmax of its current tile, so each SIMD always
-    // has one wave feeding the matrix pipe.  Tile t is stored in LDS buffer
-    // t % 3 during phase 2t - 2 (its loads were issued two phases earlier);
-    // the buffer's previous tile was last read in phase 2t - 3.
-    if (ntiles > 1) {
-      load_tile(ent, kr, vr);
-      fetch_entries(2, ent);
-    }
-    __syncthreads();
-    const int half = wave >> 2;
-    for (int p = 0; p < 2 * ntiles + 2; ++p) {
-      if ((p & 1) == 0) {
-        const int t = p / 2 + 1;
-        if (t < ntiles) {
-          store_tile(t, t % 3, kr, vr);
-          if (t + 1 < ntiles) {
-            load_tile(ent, kr, vr);
-            fetch_entries(t + 2, ent);
-          }
-        }
-      }
-      const bool x_phase = ((p & 1) == 0) == (half == 0);
-      const int j = half == 0 ? p >> 1 : (p - 1) >> 1;
-      if (x_phase) {
-        if (j >= 1 && tile_active(j - 1)) pv((j - 1) % 3);
-        if (j < ntiles && tile_active(j)) qk(j % 3);
-      } else if (j >= 0 && j < ntiles && tile_active(j)) {
-        softmax(j);
-      }
-      __syncthreads();
-    }
-#elif PKV_EXTEND_DEPTH == 2
-    // Two register sets: while tile t computes, tiles t+1 and t+2 are in
-    // flight; tile t+1 is written to LDS after tile t and its registers are
-    // refilled with tile t+3.
     u32x4_t kr2[kRowsPerThread], vr2[kRowsPerThread];
+    fetch_entries(t_first, ent);
+    load_tile(ent, kr, vr);
+    fetch_entries(t_first + 1, ent);
+    store_tile(t_first, 0, kr, vr);
     if (ntiles > 1) {
       load_tile(ent, kr, vr);                  // tile 1 -> set A
-      fetch_entries(2, ent);
+      fetch_entries(t_first + 2, ent);
     }
     if (ntiles > 2) {
       load_tile(ent, kr2, vr2);                // tile 2 -> set B
-      fetch_entries(3, ent);
+      fetch_entries(t_first + 3, ent);
     }
     __syncthreads();
-    auto step = [&](int t, u32x4_t (&ka_)[kRowsPerThread], u32x4_t (&va_)[kRowsPerThread]) {
+    auto step = [&](int i, u32x4_t (&ka_)[kRowsPerThread], u32x4_t (&va_)[kRowsPerThread]) {
+      const int t = t_first + i;
       if (tile_active(t)) {
-        qk(t & 1);
+        qk(i & 1);
         softmax(t);
-        pv(t & 1);
+        pv(i & 1);
       }
-      if (t + 1 < ntiles) {
-        store_tile(t + 1, (t + 1) & 1, ka_, va_);
-        if (t + 3 < ntiles) {
+      if (i + 1 < ntiles) {
+        store_tile(t + 1, (i + 1) & 1, ka_, va_);
+        if (i + 3 < ntiles) {
           load_tile(ent, ka_, va_);
           fetch_entries(t + 4, ent);
         }
       }
       __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, kr, vr);                         // stores tile t+1 (set A)
-      if (t + 1 >= ntiles) break;
-      step(t + 1, kr2, vr2);                   // stores tile t+2 (set B)
+    for (int i = 0; i < ntiles; i += 2) {
+      step(i, kr, vr);                         // stores tile i+1 (set A)
+      if (i + 1 >= ntiles) break;
+      step(i + 1, kr2, vr2);                   // stores tile i+2 (set B)
     }
-#else
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const bool more = t + 1 < ntiles;
-      if (more) {
-        load_tile(ent, kr, vr);
-        fetch_entries(t + 2, ent);
+  }
+
+  if (a.num_parts > 1) {
+    // Split: each valid column's state for this partition -- running max
+    // (log2 units) and sum in fp32, the output normalised by the sum in
+    // bf16 -- at workspace row ((query row) * q_heads + head) * num_parts +
+    // part.  A partition with no keys for a column leaves (-inf, 0, 0).
+#pragma unroll
+    for (int cg = 0; cg < kGroups; ++cg) {
+      const float l_tot = lsum[cg][0];
+      if (cvalid[cg]) {
+        const int col = kWaveCols * wave + 16 * cg + lc;
+        const int j = j0 + col / G;
+        const int64_t idx =
+            ((int64_t)(q0 + j) * a.q_heads + g * G + col % G) * a.num_parts + part;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + idx * kD + 4 * rg;
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db) {
+          bf16x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[cg][db][i] * inv);
+          *reinterpret_cast<bf16x4_t*>(po + 16 * db) = w;
+        }
+        if (rg == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * idx) = float2{m_run[cg], l_tot};
       }
-      if (tile_active(t)) {
-        qk(t & 1);
-        softmax(t);
-        pv(t & 1);
-      }
-      if (more) store_tile(t + 1, (t + 1) & 1, kr, vr);
-      __syncthreads();
     }
-#endif
+    return;
   }
 
 #pragma unroll
@@ -507,15 +446,56 @@ void extend_kernel(ExtendArgs a) {
   }
 }
 
+// Merge of a split call: one wave per (query row, head) of every computed
+// row; M = max_p m_p, w_p = 2^(m_p - M) l_p, out = sum_p w_p (o/l)_p /
+// sum_p w_p, in a fixed order.  Lane i owns output elements 2i, 2i + 1.
+constexpr int kMergeRowsPerWg = 4;
+
+__global__ __launch_bounds__(64 * kMergeRowsPerWg) void extend_merge_kernel(ExtendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * kMergeRowsPerWg + (threadIdx.x >> 6);
+  const int h = (int)(u % a.q_heads);
+  const int64_t rest = u / a.q_heads;
+  const int j = (int)(rest % a.max_query_len);
+  const int s = (int)(rest / a.max_query_len);
+  if (s >= a.num_seqs) return;
+  const int q0 = a.query_start[s];
+  if (q0 < 0) return;
+  const int n = min(min(a.query_start[s + 1] - q0, a.max_query_len), a.num_tokens - q0);
+  if (j >= n) return;
+  const int64_t base = ((int64_t)(q0 + j) * a.q_heads + h) * a.num_parts;
+  const float* ml = a.part_ml + 2 * base;
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o) + base * kD + 2 * lane;
+  float M = -INFINITY;
+  for (int p = 0; p < a.num_parts; ++p) M = fmaxf(M, ml[2 * p]);
+  float lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int p = 0; p < a.num_parts; ++p) {
+    const float m = ml[2 * p];
+    const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * p + 1];
+    const uint32_t o2 = *reinterpret_cast<const uint32_t*>(po + (int64_t)p * kD);
+    lsum += w;
+    acc0 = fmaf(w, __uint_as_float(o2 << 16), acc0);
+    acc1 = fmaf(w, __uint_as_float(o2 & 0xffff0000u), acc1);
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  __bf16* out = reinterpret_cast<__bf16*>(a.out) + ((int64_t)(q0 + j) * a.q_heads + h) * kD +
+                2 * lane;
+  out[0] = (__bf16)(acc0 * inv);
+  out[1] = (__bf16)(acc1 * inv);
+}
+
 template <int BS, int G>
 hipError_t launch_one(const ExtendArgs& a, hipStream_t stream) {
-  // Order 2 maps unit u to pair (u / 8 / q_tiles) * 8 + u % 8: the grid
-  // covers every pair index below num_seqs * kv_heads rounded up to 8.
+  // Unit u maps to pair (u / 8 / per_pair) * 8 + u % 8: the grid covers every
+  // pair index below num_seqs * kv_heads rounded up to 8.
   const int pairs8 = 8 * ((a.num_seqs * a.kv_heads + 7) / 8);
-  const int grid = PKV_EXTEND_ORDER == 0   ? 8 * ((a.units + 7) / 8)
-                   : PKV_EXTEND_ORDER == 1 ? a.units
-                                           : pairs8 * a.q_tiles;
+  const int grid = pairs8 * a.q_tiles * a.num_parts;
   hipLaunchKernelGGL((extend_kernel<BS, G>), dim3(grid), dim3(kThreads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.num_parts == 1) return err;
+  const int64_t rows = (int64_t)a.num_seqs * a.max_query_len * a.q_heads;
+  hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)((rows + kMergeRowsPerWg - 1) / kMergeRowsPerWg)),
+                     dim3(64 * kMergeRowsPerWg), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -22,8 +22,13 @@ struct ExtendArgs {
   int32_t q_heads;
   int32_t kv_heads;
   int32_t max_query_len;       // host bound on query_start[s+1] - query_start[s]
+  int32_t max_seq_len;         // host bound on seq_lens; keys at or past it are not read
   int32_t q_tiles;             // query tiles per (sequence, kv head)
-  int32_t units;               // num_seqs * kv_heads * q_tiles
+  int32_t units;               // num_seqs * kv_heads * q_tiles * num_parts
+  int32_t part_tokens;         // keys per partition (a multiple of 64)
+  int32_t num_parts;           // partitions per query tile (1: no split)
+  float* part_ml;              // split: [T, Hq, P, 2] (max in log2 units, sum)
+  void* part_o;                // split: [T, Hq, P, D] bf16, normalised
   uint32_t row_bytes;          // one slot: kv_heads * head_dim * element bytes
   uint32_t block_bytes;        // block_size slots
   float scale_log2;            // scale * log2(e)
@@ -39,6 +44,9 @@ struct ExtendArgs {
 // Query columns (token, head) one workgroup covers; a workgroup holds
 // kExtendCols / G query tokens of one sequence.
 constexpr int kExtendCols = PKV_EXTEND_WAVES * 16 * PKV_EXTEND_GROUPS;
+
+// Keys per LDS tile of the extend kernel: partition lengths are multiples.
+constexpr int kExtendKeys = 64;
 
 bool extend_supported(int dtype, int head_dim, int block_size, int group);
 hipError_t launch_extend(const ExtendArgs& a, int block_size, int group, hipStream_t stream);

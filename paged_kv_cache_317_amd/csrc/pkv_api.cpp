@@ -273,26 +273,105 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
                   "paged_attn_decode launch");
 }
 
+namespace {
+
+// Extend split policy.  The grid has num_seqs * kv_heads * q_tiles
+// workgroups, and one of them (8 waves at two waves per SIMD) fills a CU;
+// with fewer than kExtendUnitTarget of them and long keys, each query tile's
+// keys are cut into partitions so that the grid reaches the target, never
+// shorter than kMinExtendPart keys.
+constexpr int64_t kExtendUnitTarget = 256;
+constexpr int64_t kMinExtendPart = 1024;
+
+struct ExtendPlan {
+  int64_t q_tiles = 0;
+  int64_t part_tokens = 0;
+  int64_t num_parts = 1;
+  size_t workspace = 0;
+};
+
+pkv_status plan_extend(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_tokens,
+                       int32_t q_heads, int32_t max_query_len, int32_t max_seq_len,
+                       int32_t part_tokens, ExtendPlan* plan) {
+  pkv_status st = check_cache(c);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_seq_len < 0 || part_tokens < 0)
+    return fail(PKV_ERR_SHAPE, "num_seqs, num_tokens, max_query_len, max_seq_len and "
+                "part_tokens must be >= 0");
+  if (q_heads < 1 || q_heads % c->kv_heads)
+    return fail(PKV_ERR_SHAPE, "q_heads (%d) must be a positive multiple of kv_heads (%d)",
+                (int)q_heads, (int)c->kv_heads);
+  const int group = q_heads / c->kv_heads;
+  if (!pkv::extend_supported(c->dtype, c->head_dim, c->block_size, group))
+    return fail(PKV_ERR_UNSUPPORTED, "extend attention supports bf16 caches with head_dim 128, "
+                "block_size 16 or 32 and G in {1, 2, 4, 8} (got dtype %d, head_dim %d, "
+                "block_size %d, G %d)", (int)c->dtype, (int)c->head_dim,
+                (int)c->block_size, group);
+  const int64_t tokens_per_wg = pkv::kExtendCols / group;
+  plan->q_tiles = (max_query_len + tokens_per_wg - 1) / tokens_per_wg;
+  const int64_t keys = std::max<int64_t>(max_seq_len, 1);
+  const int64_t units = (int64_t)num_seqs * c->kv_heads * plan->q_tiles;
+  int64_t pt;
+  if (part_tokens > 0) {
+    pt = part_tokens;
+  } else if (units >= kExtendUnitTarget || keys <= kMinExtendPart || units == 0) {
+    pt = keys;
+  } else {
+    const int64_t parts = (kExtendUnitTarget + units - 1) / units;
+    pt = std::max<int64_t>((keys + parts - 1) / parts, kMinExtendPart);
+  }
+  pt = round_up(std::min<int64_t>(pt, keys), pkv::kExtendKeys);
+  if (pt > INT32_MAX / 2) return fail(PKV_ERR_SHAPE, "partition of %lld keys is too long", (long long)pt);
+  plan->part_tokens = pt;
+  plan->num_parts = (keys + pt - 1) / pt;
+  plan->workspace = 0;
+  if (plan->num_parts > 1) {
+    const int64_t rows = (int64_t)num_tokens * q_heads * plan->num_parts;
+    plan->workspace = (size_t)(round_up(2 * rows, 4) * sizeof(float) +
+                               rows * c->head_dim * elem_bytes(c->dtype));
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+PKV_EXPORT int32_t pkv_extend_partition_tokens(const pkv_cache_desc* cache, int32_t num_seqs,
+                                               int32_t num_tokens, int32_t q_heads,
+                                               int32_t max_query_len, int32_t max_seq_len,
+                                               int32_t part_tokens) {
+  ExtendPlan plan;
+  if (plan_extend(cache, num_seqs, num_tokens, q_heads, max_query_len, max_seq_len, part_tokens,
+                  &plan) != PKV_OK)
+    return 0;
+  ok();
+  return (int32_t)plan.part_tokens;
+}
+
+PKV_EXPORT size_t pkv_extend_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
+                                            int32_t num_tokens, int32_t q_heads,
+                                            int32_t max_query_len, int32_t max_seq_len,
+                                            int32_t part_tokens) {
+  ExtendPlan plan;
+  if (plan_extend(cache, num_seqs, num_tokens, q_heads, max_query_len, max_seq_len, part_tokens,
+                  &plan) != PKV_OK)
+    return 0;
+  ok();
+  return plan.workspace;
+}
+
 PKV_EXPORT pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache, const void* v_cache,
                                             const pkv_cache_desc* cache, const int32_t* block_table,
                                             int32_t table_width, const int32_t* seq_lens,
                                             const int32_t* query_start, int32_t num_seqs,
                                             int32_t num_tokens, int32_t q_heads,
-                                            int32_t max_query_len, float scale, void* out,
+                                            int32_t max_query_len, int32_t max_seq_len,
+                                            float scale, void* out, int32_t part_tokens,
+                                            void* workspace, size_t workspace_bytes,
                                             void* stream) {
-  pkv_status st = check_cache(cache);
+  ExtendPlan plan;
+  pkv_status st = plan_extend(cache, num_seqs, num_tokens, q_heads, max_query_len, max_seq_len,
+                              part_tokens, &plan);
   if (st != PKV_OK) return st;
-  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0)
-    return fail(PKV_ERR_SHAPE, "num_seqs, num_tokens and max_query_len must be >= 0");
-  if (q_heads < 1 || q_heads % cache->kv_heads)
-    return fail(PKV_ERR_SHAPE, "q_heads (%d) must be a positive multiple of kv_heads (%d)",
-                (int)q_heads, (int)cache->kv_heads);
-  const int group = q_heads / cache->kv_heads;
-  if (!pkv::extend_supported(cache->dtype, cache->head_dim, cache->block_size, group))
-    return fail(PKV_ERR_UNSUPPORTED, "extend attention supports bf16 caches with head_dim 128, "
-                "block_size 16 or 32 and G in {1, 2, 4, 8} (got dtype %d, head_dim %d, "
-                "block_size %d, G %d)", (int)cache->dtype, (int)cache->head_dim,
-                (int)cache->block_size, group);
   if (!(scale > 0.f) || !(scale < INFINITY))
     return fail(PKV_ERR_SHAPE, "scale must be positive and finite");
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return ok();
@@ -304,16 +383,26 @@ PKV_EXPORT pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache, 
                 "must be non-NULL");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (plan.workspace > 0) {
+    if (!workspace)
+      return fail(PKV_ERR_WORKSPACE, "this call splits into %lld partitions and needs a "
+                  "%zu-byte workspace", (long long)plan.num_parts, plan.workspace);
+    if (workspace_bytes < plan.workspace)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
+                  workspace_bytes, plan.workspace);
+    if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  const int group = q_heads / cache->kv_heads;
   const int64_t row_bytes = (int64_t)cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype);
   const int64_t block_bytes = row_bytes * cache->block_size;
   if (block_bytes > UINT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "a block of %lld bytes exceeds 4 GiB", (long long)block_bytes);
-  const int64_t tokens_per_wg = pkv::kExtendCols / group;
-  const int64_t q_tiles = (max_query_len + tokens_per_wg - 1) / tokens_per_wg;
-  const int64_t units = (int64_t)num_seqs * cache->kv_heads * q_tiles;
-  // The launch may round the (sequence, kv head) pairs up to a multiple of 8.
-  const int64_t grid = ((int64_t)num_seqs * cache->kv_heads + 7) / 8 * 8 * q_tiles;
-  if (grid > INT32_MAX)
+  const int64_t units = (int64_t)num_seqs * cache->kv_heads * plan.q_tiles * plan.num_parts;
+  // The launch rounds the (sequence, kv head) pairs up to a multiple of 8.
+  const int64_t grid =
+      ((int64_t)num_seqs * cache->kv_heads + 7) / 8 * 8 * plan.q_tiles * plan.num_parts;
+  const int64_t merge_rows = (int64_t)num_seqs * max_query_len * q_heads;
+  if (grid > INT32_MAX || merge_rows > (int64_t)INT32_MAX * 4)
     return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)grid);
 
   pkv::ExtendArgs a;
@@ -331,8 +420,18 @@ PKV_EXPORT pkv_status pkv_paged_attn_extend(const void* q, const void* k_cache, 
   a.q_heads = q_heads;
   a.kv_heads = cache->kv_heads;
   a.max_query_len = max_query_len;
-  a.q_tiles = (int32_t)q_tiles;
+  a.max_seq_len = std::max(max_seq_len, 1);
+  a.q_tiles = (int32_t)plan.q_tiles;
   a.units = (int32_t)units;
+  a.part_tokens = (int32_t)plan.part_tokens;
+  a.num_parts = (int32_t)plan.num_parts;
+  a.part_ml = nullptr;
+  a.part_o = nullptr;
+  if (plan.workspace > 0) {
+    const int64_t rows = (int64_t)num_tokens * q_heads * plan.num_parts;
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = a.part_ml + round_up(2 * rows, 4);
+  }
   a.row_bytes = (uint32_t)row_bytes;
   a.block_bytes = (uint32_t)block_bytes;
   a.scale_log2 = scale * 1.4426950408889634f;

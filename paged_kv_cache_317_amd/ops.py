@@ -105,7 +105,9 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale, max_seq
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", dev, q.dtype, q.shape)
-    need = decode_workspace_size(k_cache, S, Hq, max_seq_len, part_tokens)
+    # 0 on invalid arguments too: the call itself then reports them
+    need = lib().pkv_decode_workspace_size(ctypes.byref(desc), S, Hq, int(max_seq_len),
+                                           int(part_tokens))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -119,13 +121,35 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale, max_seq
     return out
 
 
+def extend_partition_tokens(k_cache, num_seqs, num_tokens, q_heads, max_query_len,
+                            max_seq_len, part_tokens=0):
+    desc = cache_desc(k_cache)
+    n = lib().pkv_extend_partition_tokens(ctypes.byref(desc), num_seqs, num_tokens, q_heads,
+                                          max_query_len, max_seq_len, part_tokens)
+    if n == 0:
+        raise ValueError(lib().pkv_last_error().decode())
+    return n
+
+
+def extend_workspace_size(k_cache, num_seqs, num_tokens, q_heads, max_query_len, max_seq_len,
+                          part_tokens=0):
+    desc = cache_desc(k_cache)
+    n = lib().pkv_extend_workspace_size(ctypes.byref(desc), num_seqs, num_tokens, q_heads,
+                                        max_query_len, max_seq_len, part_tokens)
+    if n == 0 and lib().pkv_last_error():
+        raise ValueError(lib().pkv_last_error().decode())
+    return n
+
+
 def paged_attn_extend(q, k_cache, v_cache, block_table, seq_lens, query_start, scale,
-                      max_query_len, out=None):
+                      max_query_len, max_seq_len, out=None, part_tokens=0, workspace=None):
     """Causal attention of each sequence's new tokens (prefill or chunked
     extend) over the paged cache.  ``q`` and ``out`` are packed
     ``[T, q_heads, head_dim]``; sequence ``s`` owns rows
-    ``query_start[s] .. query_start[s + 1] - 1``.  ``max_query_len`` is a
-    host-side bound on those counts.  Returns ``out``."""
+    ``query_start[s] .. query_start[s + 1] - 1``.  ``max_query_len`` and
+    ``max_seq_len`` are host-side bounds on those counts and on ``seq_lens``.
+    ``workspace`` (uint8, device) is allocated here when the call splits and
+    none is given.  Returns ``out``."""
     desc = _check_caches(k_cache, v_cache)
     dev = k_cache.device
     if q.dim() != 3:
@@ -141,11 +165,20 @@ def paged_attn_extend(q, k_cache, v_cache, block_table, seq_lens, query_start, s
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", dev, q.dtype, q.shape)
+    # 0 on invalid arguments too: the call itself then reports them
+    need = lib().pkv_extend_workspace_size(ctypes.byref(desc), S, T, Hq, int(max_query_len),
+                                           int(max_seq_len), int(part_tokens))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is not None:
+        _require(workspace, "workspace", dev)
     with torch.cuda.device(dev):
         check(lib().pkv_paged_attn_extend(
             _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_table),
             block_table.shape[1], _ptr(seq_lens), _ptr(query_start), S, T, Hq,
-            int(max_query_len), float(scale), _ptr(out), _stream(dev)))
+            int(max_query_len), int(max_seq_len), float(scale), _ptr(out), int(part_tokens),
+            _ptr(workspace), ws_bytes, _stream(dev)))
     return out
 
 

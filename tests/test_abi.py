@@ -125,9 +125,11 @@ def test_partition_request_rounds_to_block_size():
 
 
 def _extend(desc, S=2, T=40, Hq=32, maxq=20, scale=0.1, q=1 << 12, kc=1 << 12, vc=1 << 12,
-            table=1 << 12, lens=1 << 12, qs=1 << 12, out=1 << 12, width=8):
+            table=1 << 12, lens=1 << 12, qs=1 << 12, out=1 << 12, width=8, msl=128, part=0,
+            ws=None, ws_bytes=0):
     return lib().pkv_paged_attn_extend(q, kc, vc, ctypes.byref(desc) if desc else None, table,
-                                       width, lens, qs, S, T, Hq, maxq, scale, out, None)
+                                       width, lens, qs, S, T, Hq, maxq, msl, scale, out, part,
+                                       ws, ws_bytes, None)
 
 
 def test_extend_argument_checks_run_before_any_launch():
@@ -148,10 +150,44 @@ def test_extend_argument_checks_run_before_any_launch():
     assert _status(_extend(_desc(), qs=0)) == "NULL"
     assert _status(_extend(_desc(), out=(1 << 12) + 4)) == "ALIGN"
     assert _status(_extend(_desc(), width=0)) == "SHAPE"
+    assert _status(_extend(_desc(), msl=-1)) == "SHAPE"
+    assert _status(_extend(_desc(), part=-1)) == "SHAPE"
+    # a split call needs a workspace of the reported size, 16-byte aligned
+    d = _desc()
+    need = lib().pkv_extend_workspace_size(ctypes.byref(d), 2, 40, 32, 20, 4096, 256)
+    assert need > 0
+    assert _status(_extend(d, msl=4096, part=256)) == "WORKSPACE"
+    assert _status(_extend(d, msl=4096, part=256, ws=1 << 20, ws_bytes=need - 1)) == "WORKSPACE"
+    assert _status(_extend(d, msl=4096, part=256, ws=(1 << 20) + 8, ws_bytes=need)) == "ALIGN"
     # nothing to compute: OK with NULL pointers
     for kw in (dict(S=0), dict(T=0), dict(maxq=0)):
         assert _status(_extend(_desc(), q=0, kc=0, vc=0, table=0, lens=0, qs=0, out=0,
                                **kw)) == "OK"
+
+
+def test_extend_split_policy_and_workspace_size():
+    L = lib()
+    d = _desc()                                   # kv_heads 8, head_dim 128, bf16
+    part = lambda *a: L.pkv_extend_partition_tokens(ctypes.byref(d), *a)
+    size = lambda *a: L.pkv_extend_workspace_size(ctypes.byref(d), *a)
+    # G = 4: 64 tokens per query tile.  Few units and long keys: split so that
+    # about 256 units run, never below 1024 keys per partition.
+    S, T, Hq, maxq, msl = 1, 1024, 32, 1024, 65536
+    units = S * 8 * (maxq // 64)                  # 128
+    got = part(S, T, Hq, maxq, msl, 0)
+    parts = -(-256 // units)
+    assert got == max(-(-msl // parts), 1024) and got % 64 == 0
+    P = -(-msl // got)
+    rows = T * Hq * P
+    assert size(S, T, Hq, maxq, msl, 0) == -(-2 * rows // 4) * 4 * 4 + rows * 128 * 2
+    # enough units, or short keys: no split, no workspace
+    assert part(2, 2048, Hq, 1024, msl, 0) == msl
+    assert size(2, 2048, Hq, 1024, msl, 0) == 0
+    assert part(S, T, Hq, maxq, 1000, 0) == 1024 and size(S, T, Hq, maxq, 1000, 0) == 0
+    # explicit partitions round up to the 64-key tile, capped at the keys
+    assert part(S, T, Hq, maxq, msl, 100) == 128
+    assert part(S, T, Hq, maxq, 300, 100000) == 320
+    assert size(S, T, Hq, maxq, 300, 100000) == 0
 
 
 def test_block_move_argument_checks_run_before_any_launch():

@@ -31,10 +31,11 @@ def _upload(w):
     }
 
 
-def _step(d, cfg, max_query_len, out=None):
+def _step(d, cfg, max_query_len, max_seq_len, out=None, part_tokens=0):
     pkv.paged_kv_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
     out = pkv.paged_attn_extend(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
-                                d["seq_lens"], d["query_start"], cfg.scale, max_query_len, out=out)
+                                d["seq_lens"], d["query_start"], cfg.scale, max_query_len,
+                                max_seq_len, out=out, part_tokens=part_tokens)
     torch.cuda.synchronize()
     return out
 
@@ -48,22 +49,28 @@ def _oracle(w, kc=None, vc=None, seqs=None, table=None, lens=None, qs=None):
                                    seqs=seqs)
 
 
+@pytest.mark.parametrize("part_tokens", [0, 64, 192, 1024])
 @pytest.mark.parametrize("name", ["x1_extend_tiny_bf16", "x4_extend_g8_bs32_bf16",
                                   "x5_extend_mha_bf16"])
-def test_extend_matches_the_oracle(name):
+def test_extend_matches_the_oracle(name, part_tokens):
+    """Whole batches against the oracle, unsplit (0: these batches are too
+    short for the library to split) and with the keys cut into partitions of
+    64, 192 and 1024 that a merge kernel combines."""
     cfg = EXTEND_CONFIGS[name]
     w = generate_extend_host(cfg)
-    log(f"extend {name}: T={w.num_tokens} max_q={w.max_query_len} pool={w.layout.num_blocks}")
+    log(f"extend {name} part {part_tokens}: T={w.num_tokens} max_q={w.max_query_len} "
+        f"pool={w.layout.num_blocks}")
     d = _upload(w)
-    out = _step(d, cfg, w.max_query_len)
+    out = _step(d, cfg, w.max_query_len, w.max_seq_len, part_tokens=part_tokens)
     kc, vc = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
     ref = _oracle(w, kc, vc)
     mabs, mrel = compare(out, ref, cfg.dtype)
     log(f"  max-abs {mabs:.3e} row max-rel {mrel:.3e}")
 
 
-def test_extend_ignores_unused_slots_and_unreferenced_blocks():
-    """NaN in every slot no sequence uses changes nothing."""
+@pytest.mark.parametrize("part_tokens", [0, 64])
+def test_extend_ignores_unused_slots_and_unreferenced_blocks(part_tokens):
+    """NaN in every slot no sequence uses changes nothing, split or not."""
     cfg = EXTEND_CONFIGS["x1_extend_tiny_bf16"]
     w = generate_extend_host(cfg)
     kc, vc = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
@@ -79,20 +86,25 @@ def test_extend_ignores_unused_slots_and_unreferenced_blocks():
     d = _upload(w)
     d["k_cache"], d["v_cache"] = to_device(kp, "bf16"), to_device(vp, "bf16")
     out = pkv.paged_attn_extend(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
-                                d["seq_lens"], d["query_start"], cfg.scale, w.max_query_len)
+                                d["seq_lens"], d["query_start"], cfg.scale, w.max_query_len,
+                                w.max_seq_len, part_tokens=part_tokens)
     d2 = _upload(w)
     d2["k_cache"], d2["v_cache"] = to_device(kc, "bf16"), to_device(vc, "bf16")
     clean = pkv.paged_attn_extend(d2["q"], d2["k_cache"], d2["v_cache"], d2["block_table"],
-                                  d2["seq_lens"], d2["query_start"], cfg.scale, w.max_query_len)
+                                  d2["seq_lens"], d2["query_start"], cfg.scale, w.max_query_len,
+                                  w.max_seq_len, part_tokens=part_tokens)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     assert torch.equal(out.view(torch.int16), clean.view(torch.int16))
 
 
-def test_extend_degenerate_cases():
+@pytest.mark.parametrize("part_tokens", [0, 64])
+def test_extend_degenerate_cases(part_tokens):
     """Queries before position 0 and an empty sequence give zero rows; a
     sequence with no new tokens writes nothing; rows past max_query_len are
-    left as they were; a table entry outside the pool ends the sequence."""
+    left as they were; a table entry outside the pool ends the sequence.
+    Split calls give the same rows (partitions with no visible key merge to
+    nothing)."""
     cfg = EXTEND_CONFIGS["x1_extend_tiny_bf16"]
     w = generate_extend_host(cfg)
     d = _upload(w)
@@ -110,7 +122,7 @@ def test_extend_degenerate_cases():
     sentinel = torch.full_like(d["q"], 3.0)
     out = pkv.paged_attn_extend(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
                                 d["seq_lens"], d["query_start"], cfg.scale, 40,
-                                out=sentinel)
+                                int(lens.max()), out=sentinel, part_tokens=part_tokens)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     ref = _oracle(w, lens=lens, seqs=[0, 1, 2])
@@ -138,12 +150,12 @@ def test_extend_rejects_what_it_does_not_support():
     kf = d["k_cache"].float()
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_attn_extend(d["q"].float(), kf, kf, d["block_table"], d["seq_lens"],
-                              d["query_start"], cfg.scale, w.max_query_len)
+                              d["query_start"], cfg.scale, w.max_query_len, w.max_seq_len)
     assert e.value.status_name == "PKV_ERR_UNSUPPORTED"
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_attn_extend(d["q"][:, :6].contiguous(), d["k_cache"], d["v_cache"],
                               d["block_table"], d["seq_lens"], d["query_start"], cfg.scale,
-                              w.max_query_len)
+                              w.max_query_len, w.max_seq_len)
     assert e.value.status_name == "PKV_ERR_UNSUPPORTED"      # G = 3
 
 
@@ -157,7 +169,7 @@ def test_extend_full_size_sampled(name, nsample):
     d = {"q": w.q, "k_cache": w.k_cache, "v_cache": w.v_cache, "new_k": w.new_k,
          "new_v": w.new_v, "slot_mapping": w.slot_mapping, "block_table": w.block_table,
          "seq_lens": w.seq_lens, "query_start": w.query_start_dev}
-    out = _step(d, cfg, w.max_query_len)
+    out = _step(d, cfg, w.max_query_len, w.max_seq_len)
     kc, vc = to_host(w.k_cache, "bf16"), to_host(w.v_cache, "bf16")
     q = to_host(w.q, "bf16")
     rng = np.random.default_rng(7)
@@ -170,6 +182,44 @@ def test_extend_full_size_sampled(name, nsample):
     rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
     mabs, mrel = compare(out, ref, "bf16", rows=rows)
     log(f"  sequences {seqs}: max-abs {mabs:.3e} row max-rel {mrel:.3e}")
+
+
+def test_extend_long_context_split_sampled():
+    """One prompt with 40-56 k cached tokens and 1024 new ones: too few units
+    to fill the device, so the library splits the keys.  The oracle checks
+    windows of 16 consecutive queries (first, middle, last of each sequence)
+    for two kv heads: a window [a, b) of sequence s is the same problem as a
+    sequence of length ctx + b whose new tokens are those b - a queries."""
+    cfg = EXTEND_CONFIGS["x6_long_extend_bf16"]
+    w = generate_extend_device(cfg)
+    T, Hq, G = w.num_tokens, cfg.q_heads, cfg.group
+    part = pkv.extend_partition_tokens(w.k_cache, cfg.num_seqs, T, Hq, w.max_query_len,
+                                       w.max_seq_len)
+    log(f"extend long: T={T} max_len={w.max_seq_len} partition {part}")
+    assert part < w.max_seq_len
+    d = {"q": w.q, "k_cache": w.k_cache, "v_cache": w.v_cache, "new_k": w.new_k,
+         "new_v": w.new_v, "slot_mapping": w.slot_mapping, "block_table": w.block_table,
+         "seq_lens": w.seq_lens, "query_start": w.query_start_dev}
+    out = _step(d, cfg, w.max_query_len, w.max_seq_len)
+    kc, vc = to_host(w.k_cache, "bf16"), to_host(w.v_cache, "bf16")
+    q = to_host(w.q, "bf16")
+    qs, lens, table = w.query_start, w.layout.seq_lens, w.layout.block_table
+    worst = 0.0
+    for s in range(cfg.num_seqs):
+        n = int(qs[s + 1] - qs[s])
+        ctx = int(lens[s]) - n
+        for a in (0, n // 2 - 8, n - 16):
+            b = a + 16
+            for g in (0, cfg.kv_heads - 3):
+                heads = slice(g * G, (g + 1) * G)
+                ref = oracle.extend_attention(
+                    np.ascontiguousarray(q[qs[s] + a:qs[s] + b, heads]),
+                    np.ascontiguousarray(kc[:, :, g:g + 1]), np.ascontiguousarray(vc[:, :, g:g + 1]),
+                    table[s:s + 1], np.array([ctx + b]), np.array([0, b - a]), cfg.scale, "bf16")
+                got = out[qs[s] + a:qs[s] + b, heads]
+                mabs, _ = compare(got, ref, "bf16")
+                worst = max(worst, mabs)
+    log(f"  max-abs {worst:.3e}")
 
 
 def test_extend_and_block_move_replay_inside_a_captured_graph():
@@ -190,7 +240,7 @@ def test_extend_and_block_move_replay_inside_a_captured_graph():
         pkv.paged_kv_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
         pkv.paged_attn_extend(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
                               d["seq_lens"], d["query_start"], cfg.scale, w.max_query_len,
-                              out=out)
+                              w.max_seq_len, out=out)
         pkv.paged_block_move(pairs, d["k_cache"], d["v_cache"], host_k, host_v)
 
     step()

@@ -82,12 +82,14 @@ def test_extend_random_shapes(seed):
     T = int(qs[-1])
     q = _values(rng, (max(T, 1), Hkv * G, 128), "bf16")[:T]
     scale = float(rng.uniform(0.02, 0.2))
-    log(f"extend seed {seed}: S={S} T={T} BS={BS} Hkv={Hkv} G={G}")
+    part = int(rng.choice([0, 0, 64, 128, 320, 1024]))
+    log(f"extend seed {seed}: S={S} T={T} BS={BS} Hkv={Hkv} G={G} part={part}")
     if T == 0:
         pytest.skip("no new tokens drawn")
     out = pkv.paged_attn_extend(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
                                 to_device(table, None), to_device(lens.astype(np.int32), None),
-                                to_device(qs, None), scale, int(new.max()))
+                                to_device(qs, None), scale, int(new.max()), int(lens.max()),
+                                part_tokens=part)
     torch.cuda.synchronize()
     ref = oracle.extend_attention(q, kc, vc, table, lens, qs, scale, "bf16")
     compare(out, ref, "bf16")

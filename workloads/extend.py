@@ -86,6 +86,13 @@ EXTEND_CONFIGS = {
         name="x5_extend_mha_bf16", num_seqs=4, q_heads=16, kv_heads=16, head_dim=128,
         block_size=16, dtype="bf16", std=1.0, seed=317_105,
         ctx_range=(0, 500), new_range=(1, 200), max_len=700),
+    # Chunked extend of one long prompt: 1024 new tokens on 40-56 k cached
+    # tokens, too few (sequence, kv head, query tile) units to fill the device
+    # without splitting the keys.
+    "x6_long_extend_bf16": ExtendConfig(
+        name="x6_long_extend_bf16", num_seqs=1, q_heads=32, kv_heads=8, head_dim=128,
+        block_size=16, dtype="bf16", std=1.0, seed=317_106,
+        ctx_range=(40960, 57344), new_range=(1024, 1024), max_len=58368),
 }
 
 
@@ -116,6 +123,10 @@ class ExtendWorkload:
     @property
     def max_query_len(self):
         return int(np.diff(self.query_start).max(initial=0))
+
+    @property
+    def max_seq_len(self):
+        return int(np.asarray(self.layout.seq_lens).max(initial=0))
 
 
 def _lengths(rng, fixed, rng_range, S):
