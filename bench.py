@@ -88,6 +88,7 @@ EXTEND_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_extend.hip",
 PROFILES = {
     DEFAULT_WORKLOAD: ("paged_attn_decode_c3_gqa4k_bf16.md", DECODE_SOURCES),
     "x3_extend_bf16": ("paged_attn_extend_x3_extend_bf16.md", EXTEND_SOURCES),
+    "x6_long_extend_bf16": ("paged_attn_extend_x6_long_extend_bf16.md", EXTEND_SOURCES),
 }
 
 
@@ -328,6 +329,7 @@ def prefix_cache_report(cfg, lay):
 
 
 EXTEND_METRIC = "paged prefill/extend attention: causal TFLOP/s, 1 GPU"
+CPU_EXTEND_FLOPS = 2.5e11
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 
 
@@ -412,10 +414,19 @@ def extend_bench(args):
     cpu = None
     if args.cpu_sample > 0:
         import oracle
-        # A bounded sample: the new tokens (at most 1024) of the shortest sequence.
+        # A bounded sample: the first new tokens of the shortest sequence, as
+        # many as keep the causal work near CPU_EXTEND_FLOPS (10-30 s of the
+        # fp64 oracle on one core).
         s = int(np.argmin(lay.seq_lens))
         qs = w.query_start
-        nq = min(int(qs[s + 1] - qs[s]), 1024)
+        n_new = int(qs[s + 1] - qs[s])
+        ctx = int(lay.seq_lens[s]) - n_new
+        nq = 1
+        while nq < min(n_new, 1024) and causal_work(
+                np.array([ctx + 2 * nq]), np.array([0, 2 * nq]), cfg.q_heads,
+                cfg.head_dim)[0] <= CPU_EXTEND_FLOPS:
+            nq *= 2
+        nq = min(nq, n_new)
         q = host_array(w.q)[qs[s]:qs[s] + nq]
         kc, vc = host_array(w.k_cache), host_array(w.v_cache)
         L = int(lay.seq_lens[s])
