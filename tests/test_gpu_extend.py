@@ -143,6 +143,31 @@ def test_extend_degenerate_cases(part_tokens):
         compare(torch.from_numpy(got[r:r + 1]), row, "bf16")
 
 
+@pytest.mark.parametrize("part_tokens", [0, 64])
+def test_extend_max_seq_len_cuts_the_keys(part_tokens):
+    """A max_seq_len below some lengths cuts those sequences' keys: the query
+    at position p sees keys 0 .. min(p + 1, max_seq_len) - 1 (positions keep
+    their uncut values); the oracle computes each row as one query over a
+    sequence of that many keys."""
+    cfg = EXTEND_CONFIGS["x1_extend_tiny_bf16"]
+    w = generate_extend_host(cfg)
+    cut = 72
+    assert w.max_seq_len > cut
+    d = _upload(w)
+    out = _step(d, cfg, w.max_query_len, cut, part_tokens=part_tokens)
+    kc, vc = oracle.kv_write(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping)
+    qs, lens = w.query_start, w.seq_lens
+    got = out.float().cpu().numpy()
+    for s in range(cfg.num_seqs):
+        n = int(qs[s + 1] - qs[s])
+        for j in range(n):
+            r = int(qs[s]) + j
+            keys = min(int(lens[s]) - n + j + 1, cut)
+            row = oracle.extend_attention(w.q[r:r + 1], kc, vc, w.block_table[s:s + 1],
+                                          np.array([keys]), np.array([0, 1]), cfg.scale, "bf16")
+            compare(torch.from_numpy(got[r:r + 1]), row, "bf16")
+
+
 def test_extend_rejects_what_it_does_not_support():
     cfg = EXTEND_CONFIGS["x1_extend_tiny_bf16"]
     w = generate_extend_host(cfg)
@@ -159,17 +184,19 @@ def test_extend_rejects_what_it_does_not_support():
     assert e.value.status_name == "PKV_ERR_UNSUPPORTED"      # G = 3
 
 
-@pytest.mark.parametrize("name,nsample", [("x2_prefill_bf16", 3), ("x3_extend_bf16", 4)])
-def test_extend_full_size_sampled(name, nsample):
+@pytest.mark.parametrize("name,nsample,part", [("x2_prefill_bf16", 3, 0), ("x3_extend_bf16", 4, 0),
+                                               ("x3_extend_bf16", 2, 1024)])
+def test_extend_full_size_sampled(name, nsample, part):
     """Full-size batches drawn on the device; the oracle computes a seeded
-    sample of sequences (plus the longest) from the pools copied back."""
+    sample of sequences (plus the longest) from the pools copied back.  The
+    chunked-extend batch also runs split into 1024-key partitions."""
     cfg = EXTEND_CONFIGS[name]
     w = generate_extend_device(cfg)
-    log(f"extend full {name}: T={w.num_tokens} pool={w.layout.num_blocks}")
+    log(f"extend full {name} part {part}: T={w.num_tokens} pool={w.layout.num_blocks}")
     d = {"q": w.q, "k_cache": w.k_cache, "v_cache": w.v_cache, "new_k": w.new_k,
          "new_v": w.new_v, "slot_mapping": w.slot_mapping, "block_table": w.block_table,
          "seq_lens": w.seq_lens, "query_start": w.query_start_dev}
-    out = _step(d, cfg, w.max_query_len, w.max_seq_len)
+    out = _step(d, cfg, w.max_query_len, w.max_seq_len, part_tokens=part)
     kc, vc = to_host(w.k_cache, "bf16"), to_host(w.v_cache, "bf16")
     q = to_host(w.q, "bf16")
     rng = np.random.default_rng(7)
