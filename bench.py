@@ -87,6 +87,7 @@ EXTEND_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_extend.hip",
 # record count only while the kernel sources hash to the recorded value.
 PROFILES = {
     DEFAULT_WORKLOAD: ("paged_attn_decode_c3_gqa4k_bf16.md", DECODE_SOURCES),
+    "c5_long_bf16": ("paged_attn_decode_c5_long_bf16.md", DECODE_SOURCES),
     "x3_extend_bf16": ("paged_attn_extend_x3_extend_bf16.md", EXTEND_SOURCES),
     "x6_long_extend_bf16": ("paged_attn_extend_x6_long_extend_bf16.md", EXTEND_SOURCES),
 }
@@ -483,7 +484,8 @@ def extend_bench(args):
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "flops_per_launch": flops,
             "kv_bytes_per_launch": kv_bytes + io_bytes,
-            "traffic": profiled_traffic(cfg.name),
+            # the summaries were taken at the library's own partition choice
+            "traffic": profiled_traffic(cfg.name) if not args.part_tokens else None,
         },
         "cpu_baseline": cpu,
     }
@@ -616,7 +618,8 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "bytes_per_launch": roof_bytes,
-            "traffic": profiled_traffic(cfg.name),
+            # the summaries were taken at each batch's own partition length
+            "traffic": profiled_traffic(cfg.name) if args.part_tokens is None else None,
         },
         "cpu_baseline": cpu,
         "ops": ops,
