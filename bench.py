@@ -51,6 +51,7 @@ def parse_args(argv=None):
     p.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                    help="instead of the decode step, time a plain device-to-device copy of "
                         "GIB GiB (the reference kernel for HBM byte counters)")
+    p.add_argument("--cpu-oracle", default=None, help=argparse.SUPPRESS)
     return p.parse_args(argv)
 
 
@@ -142,30 +143,131 @@ def host_array(t):
     return t.numpy()
 
 
-def cpu_baseline(cfg, q, k_cache, v_cache, table, lens, nseq):
-    """The oracle, single-threaded BLAS, on the first ``nseq`` sequences."""
+def host_workers():
+    """Worker count for the oracle timing: the visible cores, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+# The oracle's timing runs in a child Python process (this one has the GPU
+# open; a fresh child does not inherit it), which forks one worker process
+# per visible core.  The inputs travel as .npy files in memory-backed
+# storage and are memory-mapped by the child and its workers.
+_ORACLE = {}
+
+
+def _oracle_task(share):
+    """One worker's share: decode sequence indices, or extend query windows
+    [lo, hi)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
-
-    nseq = min(nseq, cfg.num_seqs)
-    seqs = list(range(nseq))
+    a, job = _ORACLE["arrays"], _ORACLE["job"]
     with threadpool_limits(limits=1):
+        if job["kind"] == "decode":
+            oracle.decode_attention(a["q"], a["k_cache"], a["v_cache"], a["table"], a["lens"],
+                                    job["scale"], job["dtype"], seqs=share)
+        else:
+            for lo, hi in share:
+                # queries [lo, hi) are the new tokens of a sequence of length ctx0 + hi
+                oracle.extend_attention(a["q"][lo:hi], a["k_cache"], a["v_cache"], a["table"],
+                                        np.array([job["ctx0"] + hi]), np.array([0, hi - lo]),
+                                        job["scale"], job["dtype"])
+    return len(share)
+
+
+def _noop(_):
+    return 0
+
+
+def cpu_oracle_child(job_path):
+    """Child-process side: time the oracle on every worker, then on one core;
+    prints one JSON line."""
+    import multiprocessing as mp
+    import numpy as np
+    job = json.load(open(job_path))
+    d = job["dir"]
+    _ORACLE["job"] = job
+    _ORACLE["arrays"] = {k: np.load(os.path.join(d, k + ".npy"), mmap_mode="r")
+                         for k in job["arrays"]}
+    items = job["items"]
+    workers = job["workers"]
+    shares = [items[i::workers] for i in range(workers)]
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_noop, range(workers))            # workers started before the clock
         t0 = time.perf_counter()
-        oracle.decode_attention(q, k_cache, v_cache, table, lens, cfg.scale, cfg.dtype, seqs=seqs)
-        dt = time.perf_counter() - t0
+        pool.map(_oracle_task, shares, chunksize=1)
+        multi = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _oracle_task(job.get("whole", items))
+    one = time.perf_counter() - t0
+    print(json.dumps({"multi_s": multi, "one_s": one, "workers": workers}), flush=True)
+    return 0
+
+
+def run_cpu_oracle(kind, arrays, items, **job):
+    """Parent side: hand the arrays to a child process and return its
+    timings ({"multi_s", "one_s", "workers"})."""
+    import shutil
+    import subprocess
+    import tempfile
+    import numpy as np
+    base = "/dev/shm" if os.access("/dev/shm", os.W_OK) else None
+    d = tempfile.mkdtemp(prefix="pkv_oracle_", dir=base)
+    try:
+        for k, v in arrays.items():
+            np.save(os.path.join(d, k + ".npy"), np.ascontiguousarray(v))
+        job.update(kind=kind, dir=d, arrays=list(arrays), items=items,
+                   workers=min(host_workers(), len(items)))
+        path = os.path.join(d, "job.json")
+        with open(path, "w") as f:
+            json.dump(job, f)
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-oracle", path],
+                             capture_output=True, text=True, timeout=900)
+        if res.returncode != 0:
+            raise RuntimeError(f"oracle timing failed ({res.returncode}): {res.stderr[-2000:]}")
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def cpu_baseline(cfg, q, k_cache, v_cache, table, lens, nseq):
+    """The oracle on the first ``nseq`` sequences of the batch: one worker
+    process per visible core (one BLAS thread each, the sequences dealt out
+    in turn), then one core."""
+    import numpy as np
+    nseq = min(nseq, cfg.num_seqs)
+    t = run_cpu_oracle("decode", {"q": q, "k_cache": k_cache, "v_cache": v_cache,
+                                  "table": table, "lens": np.asarray(lens)},
+                       list(range(nseq)), scale=float(cfg.scale), dtype=cfg.dtype)
+    dt, dt1, workers = t["multi_s"], t["one_s"], t["workers"]
     sub = np.asarray(lens[:nseq], dtype=np.int64)
     kv = int(sub.sum()) * cfg.kv_heads * cfg.head_dim * cfg.elem_bytes * 2
     return {
         "value": round(kv / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
         "seqs_per_s": round(nseq / dt, 3),
         "wall_s": round(dt, 3),
+        "one_core": {"value": round(kv / dt1 / 1e9, 4), "seqs_per_s": round(nseq / dt1, 3),
+                     "wall_s": round(dt1, 3)},
         "sample": f"first {nseq} of {cfg.num_seqs} sequences of the same batch (same pools), "
-                  f"one decode step, fp64 numpy, BLAS limited to 1 thread",
+                  f"one decode step, fp64 numpy; {workers} worker processes with one BLAS "
+                  f"thread each, then one core",
     }
+
+
+def percentiles(ms):
+    """p10 / median / p90 of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 5),
+            "p50": round(float(np.percentile(a, 50)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
 
 
 def time_cache_ops(pkv, w, cfg, dev, per_graph=100, replays=5):
@@ -330,6 +432,7 @@ def prefix_cache_report(cfg, lay):
 
 
 EXTEND_METRIC = "paged prefill/extend attention: causal TFLOP/s, 1 GPU"
+FLUSH_BYTES = 1 << 30      # written between cold iterations to evict L2 and Infinity Cache
 CPU_EXTEND_FLOPS = 2.5e11
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 
@@ -402,7 +505,8 @@ def extend_bench(args):
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_list = [a.elapsed_time(b) for a, b in ev]
+    attn_ms = float(np.mean(attn_list))
     step_ms = wall * 1e3 / K
     print(f"# {K} steps: {step_ms:.4f} ms/step, extend {attn_ms:.4f} ms", file=sys.stderr,
           flush=True)
@@ -414,7 +518,6 @@ def extend_bench(args):
 
     cpu = None
     if args.cpu_sample > 0:
-        import oracle
         # A bounded sample: the first new tokens of the shortest sequence, as
         # many as keep the causal work near CPU_EXTEND_FLOPS (10-30 s of the
         # fp64 oracle on one core).
@@ -435,16 +538,26 @@ def extend_bench(args):
         # the sample's own sequence: its first nq queries at their true positions
         lens = np.array([L - n_all + nq])
         sflops, _ = causal_work(lens, np.array([0, nq]), cfg.q_heads, cfg.head_dim)
-        import threadpoolctl
-        with threadpoolctl.threadpool_limits(1):
-            t1 = time.perf_counter()
-            oracle.extend_attention(q, kc, vc, lay.block_table[s:s + 1], lens,
-                                    np.array([0, nq]), cfg.scale, cfg.dtype)
-            dt = time.perf_counter() - t1
-        cpu = {"value": round(sflops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+        # One window of consecutive queries per worker, cut so that each
+        # sees about the same number of keys; the one-core run is the whole
+        # sample in one call.
+        ctx0 = L - n_all
+        nwin = min(host_workers(), nq)
+        work = np.cumsum(ctx0 + np.arange(nq) + 1, dtype=np.float64)
+        cuts = [0] + [int(np.searchsorted(work, work[-1] * k / nwin)) + 1
+                      for k in range(1, nwin)] + [nq]
+        windows = [[a, b] for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+        t = run_cpu_oracle("extend", {"q": q, "k_cache": kc, "v_cache": vc,
+                                      "table": lay.block_table[s:s + 1]},
+                           windows, scale=float(cfg.scale),
+                           dtype=cfg.dtype, ctx0=ctx0, whole=[[0, nq]])
+        dt, dt1, workers = t["multi_s"], t["one_s"], t["workers"]
+        cpu = {"value": round(sflops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
                "kind": "oracle", "wall_s": round(dt, 3),
+               "one_core": {"value": round(sflops / dt1 / 1e12, 6), "wall_s": round(dt1, 3)},
                "sample": f"first {nq} new tokens of sequence {s} (length {L}) of the same "
-                         f"batch, fp64 numpy, BLAS limited to 1 thread"}
+                         f"batch, fp64 numpy; {workers} worker processes, one window of "
+                         f"consecutive queries each, one BLAS thread each; then one core"}
 
     line = {
         "metric": EXTEND_METRIC,
@@ -475,6 +588,7 @@ def extend_bench(args):
         },
         "tokens_per_s": round(T / (step_ms * 1e-3), 1),
         "extend_ms": round(attn_ms, 5),
+        "extend_timing_ms": percentiles(attn_list),
         "roofline": {
             "bound": "mfma",
             "kernel": "paged_attn_extend",
@@ -501,6 +615,8 @@ def main(argv=None):
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
+    if args.cpu_oracle:
+        return cpu_oracle_child(args.cpu_oracle)
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe, args.steps, args.warmup)
 
@@ -559,10 +675,24 @@ def main(argv=None):
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    warm_ms = [a.elapsed_time(b) for a, b in ev]
+    decode_ms = float(np.mean(warm_ms))
     step_ms = wall * 1e3 / K
     print(f"# {K} steps: {step_ms:.4f} ms/step, decode {decode_ms:.4f} ms", file=sys.stderr,
           flush=True)
+
+    # Cold figure, outside the timed steps: before each decode a 1 GiB write
+    # evicts the L2 and the Infinity Cache.
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    for i in range(K):
+        write()
+        flush.fill_(i & 255)
+        ev[i][0].record()
+        decode()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    cold_ms = [a.elapsed_time(b) for a, b in ev]
+    del flush
 
     nb = step_bytes(cfg, lay.seq_lens)
     step_total = nb["decode"] + nb["kv_write"]
@@ -572,6 +702,14 @@ def main(argv=None):
     # sequence).
     roof_bytes = nb["decode"] - nb["shared_repeat"]
     achieved = roof_bytes / (decode_ms * 1e-3) / 1e9
+    warm = percentiles(warm_ms)
+    cold = percentiles(cold_ms)
+    decode_stats = {
+        "warm_ms": warm, "cold_ms": cold,
+        "warm_GBps_median": round(roof_bytes / (warm["p50"] * 1e-3) / 1e9, 1),
+        "cold_GBps_median": round(roof_bytes / (cold["p50"] * 1e-3) / 1e9, 1),
+        "flush_bytes": FLUSH_BYTES,
+    }
 
     ops = time_cache_ops(pkv, w, cfg, dev)
 
@@ -610,6 +748,7 @@ def main(argv=None):
         "seqs_per_s": round(cfg.num_seqs / (step_ms * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_ms": round(decode_ms, 5),
+        "decode_timing": decode_stats,
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attn_decode" + (" (partition + merge)" if part < max_len else ""),
