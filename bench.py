@@ -89,6 +89,9 @@ EXTEND_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_extend.hip",
 PROFILES = {
     DEFAULT_WORKLOAD: ("paged_attn_decode_c3_gqa4k_bf16.md", DECODE_SOURCES),
     "c5_long_bf16": ("paged_attn_decode_c5_long_bf16.md", DECODE_SOURCES),
+    "c1_tiny_f32": ("paged_attn_decode_c1_tiny_f32.md", DECODE_SOURCES),
+    "c2_mha_bf16": ("paged_attn_decode_c2_mha_bf16.md", DECODE_SOURCES),
+    "c4_prefix_bf16": ("paged_attn_decode_c4_prefix_bf16.md", DECODE_SOURCES),
     "x3_extend_bf16": ("paged_attn_extend_x3_extend_bf16.md", EXTEND_SOURCES),
     "x6_long_extend_bf16": ("paged_attn_extend_x6_long_extend_bf16.md", EXTEND_SOURCES),
 }
