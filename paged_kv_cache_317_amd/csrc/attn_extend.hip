@@ -31,7 +31,7 @@
 //
 // Per tile and wave (bf16, head_dim 128):
 //   S^T = K Q^T   v_mfma_f32_16x16x32_bf16; keys are the M rows (A operand,
-//                 read from the padded K tile in LDS), the 16 columns of a
+//                 read from the K tile in LDS), the 16 columns of a
 //                 group the N columns (B operand, held in registers for the
 //                 whole call).  Lane (r, c) gets keys 4r..4r+3 of column c
 //                 for each 16-key block.
@@ -44,11 +44,13 @@
 //   O^T += V^T P^T  v_mfma_f32_16x16x32_bf16 with the 32 keys of two 16-key
 //                 blocks as the K dimension in the order that matches the
 //                 logits' lane layout: P stays in its lanes (rounded to
-//                 bf16), V^T comes from the padded V tile through
+//                 bf16), V^T comes from the V tile through
 //                 ds_read_b64_tr_b16 transpose reads, shared by both groups.
-// Loads: the next tile's K and V rows (16 bytes per lane, 16 lanes per
-// 256-byte row) are issued before the current tile is computed and written
-// to the other LDS buffer after it; one barrier per tile.
+// Loads: the next tile's K and V rows go straight from global memory into
+// the other LDS buffer (global_load_lds_dwordx4, 16 bytes per lane, 1 KB
+// per wave instruction) while the current tile computes; one barrier per
+// tile.  The LDS rows are unpadded and their 16-byte chunks XOR-swizzled by
+// row, which keeps both operand reads free of bank conflicts.
 #include "device_common.hpp"
 #include "extend.hpp"
 
@@ -67,21 +69,12 @@ constexpr int kStep = kThreads / 16;     // K/V rows one pass of the workgroup l
 constexpr int kRowsPerThread = kKeys / kStep;
 constexpr int kGroups = PKV_EXTEND_GROUPS;   // 16-column groups per wave
 constexpr int kWaveCols = 16 * kGroups;
-#ifndef PKV_EXTEND_KPAD
-#define PKV_EXTEND_KPAD 16
-#endif
-#ifndef PKV_EXTEND_VPAD
-#define PKV_EXTEND_VPAD 32
-#endif
-constexpr int kKRow = kD * 2 + PKV_EXTEND_KPAD;   // padded LDS row of the K tile (bytes)
-constexpr int kVRow = kD * 2 + PKV_EXTEND_VPAD;   // padded LDS row of the V tile (bytes)
-constexpr int kKTile = kKeys * kKRow;
+constexpr int kRow = kD * 2;             // LDS row of a K or V tile (bytes, unpadded)
+constexpr int kTile = kKeys * kRow;
 constexpr float kLazyLog2 = 8.f;         // running-max slack before O is rescaled
-constexpr int kVTile = kKeys * kVRow;
 static_assert(kExtendCols == kWaves * 16 * kGroups, "kWaves waves of kGroups 16-column groups");
 static_assert(kKeys % kStep == 0, "whole rows per thread");
-
-constexpr int kBufs = 2;   // LDS tile buffers
+static_assert(kStep % 16 == 0, "a load pass keeps every row's index mod 16");
 
 #ifndef PKV_EXTEND_WAVES_PER_EU
 #define PKV_EXTEND_WAVES_PER_EU 2
@@ -96,6 +89,14 @@ __device__ __forceinline__ bf16x4_t tr_read(const char* lds, int byte_off) {
       (lds_bf16x4_t*)((__attribute__((address_space(3))) char*)lds + byte_off));
 }
 
+// The 16-byte chunks of LDS row r are stored at chunk ^ chunk_swizzle(r).
+// The LDS rows are unpadded (the tile loads write whole 1 KB runs), so
+// without it the K operand reads (16 rows at one chunk) and the V transpose
+// reads (4 rows x 2 adjacent chunks per 16 lanes) would hit the same banks.
+// Of the XOR patterns measured this one was fastest; leaving it out halves
+// the kernel's speed.
+__device__ __forceinline__ int chunk_swizzle(int r) { return (r & 15) ^ ((r >> 2) & 3); }
+
 template <int BS, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_EXTEND_WAVES_PER_EU)))
 void extend_kernel(ExtendArgs a) {
@@ -103,8 +104,15 @@ void extend_kernel(ExtendArgs a) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "G in {1, 2, 4, 8}");
   constexpr int kTokens = kExtendCols / G;       // query tokens per workgroup
 
-  __shared__ __attribute__((aligned(16))) char s_k[kBufs][kKTile];
-  __shared__ __attribute__((aligned(16))) char s_v[kBufs][kVTile];
+  // Two tile buffers, one LDS object each: the compiler then sees that the
+  // loads streaming into one buffer do not touch the other, and adds no
+  // wait for them before reading it.
+  __shared__ __attribute__((aligned(16))) char s_k0[kTile];
+  __shared__ __attribute__((aligned(16))) char s_k1[kTile];
+  __shared__ __attribute__((aligned(16))) char s_v0[kTile];
+  __shared__ __attribute__((aligned(16))) char s_v1[kTile];
+  char* const s_k[2] = {s_k0, s_k1};
+  char* const s_v[2] = {s_v0, s_v1};
   __shared__ int s_first_bad;
 
   // (sequence, kv head) pairs go round-robin over the XCDs (workgroup b runs
@@ -184,10 +192,14 @@ void extend_kernel(ExtendArgs a) {
   const int qmin_w = ctx + min(j0 + (kWaveCols * wave) / G, j1 - 1);
   const int qmax_w = ctx + min(j0 + (kWaveCols * wave + kWaveCols - 1) / G, j1 - 1);
 
-  // Tile loader: thread t moves chunk t % 16 of rows t / 16 + 16 i.
+  // Tile loader: each wave instruction moves 4 rows (1 KB) straight from
+  // global memory into LDS; lane l of wave w writes the l-th 16 bytes of
+  // rows 4 w .. 4 w + 3 (+ kStep i), i.e. row lrow = l / 16 + 4 w, physical
+  // chunk lchunk = l % 16, so it fetches the logical chunk lchunk ^ swizzle.
   const int lchunk = threadIdx.x & 15;
   const int lrow = threadIdx.x >> 4;
-  const uint32_t lane_off = (uint32_t)(g * kD * 2 + 16 * lchunk);
+  const uint32_t lane_off =
+      (uint32_t)(g * kD * 2 + 16 * (lchunk ^ chunk_swizzle(lrow & 15)));
   const char* kcache = reinterpret_cast<const char*>(a.k_cache);
   const char* vcache = reinterpret_cast<const char*>(a.v_cache);
 
@@ -202,36 +214,35 @@ void extend_kernel(ExtendArgs a) {
     for (int i = 0; i < kRowsPerThread; ++i)
       e[i] = trow[min((tile * kKeys + wave_row + kStep * i) / BS, last_blk)];
   };
-  auto load_tile = [&](const int (&e)[kRowsPerThread], u32x4_t (&kr)[kRowsPerThread],
-                       u32x4_t (&vr)[kRowsPerThread]) {
+  auto load_tile = [&](const int (&e)[kRowsPerThread], int buf) {
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
       const uint32_t phys = (uint32_t)uniform_int(e[i]);
       const uint64_t base = (uint64_t)phys * a.block_bytes;
-      uint32_t off = (uint32_t)(((lrow + kStep * i) % BS) * a.row_bytes) + lane_off;
-      asm volatile("" : "+v"(off));
-      kr[i] = *reinterpret_cast<const u32x4_t*>(kcache + base + off);
-      vr[i] = *reinterpret_cast<const u32x4_t*>(vcache + base + off);
+      const uint32_t off = (uint32_t)(((lrow + kStep * i) % BS) * a.row_bytes) + lane_off;
+      const int lds_row = uniform_int(wave_row + kStep * i);
+      __builtin_amdgcn_global_load_lds(
+          kcache + base + off,
+          (__attribute__((address_space(3))) void*)(s_k[buf] + lds_row * kRow), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          vcache + base + off,
+          (__attribute__((address_space(3))) void*)(s_v[buf] + lds_row * kRow), 16, 0, 0);
     }
   };
-  // Rows at or past kv_hi (only in the last tile) are stored as zeros: they
-  // may be unused slots holding any bits.
-  auto store_tile = [&](int tile, int buf, u32x4_t (&kr)[kRowsPerThread],
-                        u32x4_t (&vr)[kRowsPerThread]) {
+  // Once this lane's loads of `tile` have landed: the rows it loaded at or
+  // past kv_hi (only in the last tile) become zeros; they may be unused
+  // slots holding any bits.
+  auto zero_tail = [&](int tile, int buf) {
     const int t0 = tile * kKeys;
     if (uniform_int(t0 + kKeys > kv_hi ? 1 : 0)) {
 #pragma unroll
       for (int i = 0; i < kRowsPerThread; ++i) {
         if (t0 + lrow + kStep * i >= kv_hi) {
-          kr[i] = u32x4_t{0u, 0u, 0u, 0u};
-          vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+          const int at = (lrow + kStep * i) * kRow + 16 * lchunk;
+          *reinterpret_cast<u32x4_t*>(s_k[buf] + at) = u32x4_t{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4_t*>(s_v[buf] + at) = u32x4_t{0u, 0u, 0u, 0u};
         }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      *reinterpret_cast<u32x4_t*>(&s_k[buf][(lrow + kStep * i) * kKRow + 16 * lchunk]) = kr[i];
-      *reinterpret_cast<u32x4_t*>(&s_v[buf][(lrow + kStep * i) * kVRow + 16 * lchunk]) = vr[i];
     }
   };
 
@@ -251,8 +262,20 @@ void extend_kernel(ExtendArgs a) {
   }
 
   // Per-lane LDS offsets of the operand reads.
-  const int ka_lane = lc * kKRow + 16 * rg;                        // K row lc, chunk rg
-  const int tr_lane = (4 * rg + (lc >> 2)) * kVRow + 8 * (lc & 3);  // V transpose read
+  // Swizzled rows: K chunk rg + 4 ks of row lc; V bytes 8 (lc & 3) + 32 db of
+  // row 4 rg + lc / 4, i.e. chunk 2 db + (lc & 3) / 2, 8 (lc & 1) bytes in.
+  // Blocks of 16 rows keep the row index mod 16, hence the swizzle.
+  int ka_off[4], tr_off[kD / 16];
+  {
+    const int sk = chunk_swizzle(lc);
+    const int vrow = 4 * rg + (lc >> 2);
+    const int sv = chunk_swizzle(vrow);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka_off[ks] = lc * kRow + 16 * ((rg + 4 * ks) ^ sk);
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db)
+      tr_off[db] = vrow * kRow + 16 * ((2 * db + ((lc & 3) >> 1)) ^ sv) + 8 * (lc & 1);
+  }
 
   // The three stages of a tile.  A wave whose columns all sit before the
   // tile (tile_active false) skips all three.
@@ -267,7 +290,7 @@ void extend_kernel(ExtendArgs a) {
       u32x4_t ka[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4_t*>(kt + ka_lane + 16 * kb * kKRow + 64 * ks);
+        ka[ks] = *reinterpret_cast<const u32x4_t*>(kt + ka_off[ks] + 16 * kb * kRow);
 #pragma unroll
       for (int cg = 0; cg < kGroups; ++cg) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -338,8 +361,8 @@ void extend_kernel(ExtendArgs a) {
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
       for (int db = 0; db < kD / 16; ++db) {
-        const bf16x4_t a0 = tr_read(vt, tr_lane + 32 * kp * kVRow + 32 * db);
-        const bf16x4_t a1 = tr_read(vt, tr_lane + (32 * kp + 16) * kVRow + 32 * db);
+        const bf16x4_t a0 = tr_read(vt, tr_off[db] + 32 * kp * kRow);
+        const bf16x4_t a1 = tr_read(vt, tr_off[db] + (32 * kp + 16) * kRow);
         const bf16x8_t av = cat(a0, a1);
 #pragma unroll
         for (int cg = 0; cg < kGroups; ++cg)
@@ -356,45 +379,42 @@ void extend_kernel(ExtendArgs a) {
   };
 
   if (ntiles > 0) {
-    // Two register sets: while tile t computes, tiles t+1 and t+2 are in
-    // flight; tile t+1 is written to LDS after tile t, one barrier per tile.
-    // Local tile i is absolute tile t_first + i, in LDS buffer i & 1.
+    // Tile i+1 streams into LDS buffer (i+1) & 1 while tile i computes; that
+    // buffer held tile i-1, released by the previous barrier.  The end of
+    // step i waits for this wave's loads, clears the tail rows it loaded,
+    // and the barrier publishes the tile.  Local tile i is absolute tile
+    // t_first + i.
     int ent[kRowsPerThread];
-    u32x4_t kr[kRowsPerThread], vr[kRowsPerThread];
-    u32x4_t kr2[kRowsPerThread], vr2[kRowsPerThread];
     fetch_entries(t_first, ent);
-    load_tile(ent, kr, vr);
+    load_tile(ent, 0);
     fetch_entries(t_first + 1, ent);
-    store_tile(t_first, 0, kr, vr);
-    if (ntiles > 1) {
-      load_tile(ent, kr, vr);                  // tile 1 -> set A
-      fetch_entries(t_first + 2, ent);
-    }
-    if (ntiles > 2) {
-      load_tile(ent, kr2, vr2);                // tile 2 -> set B
-      fetch_entries(t_first + 3, ent);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
+    zero_tail(t_first, 0);
     __syncthreads();
-    auto step = [&](int i, u32x4_t (&ka_)[kRowsPerThread], u32x4_t (&va_)[kRowsPerThread]) {
+    // Unrolled by two so that every buffer index is a constant.
+    auto step = [&](int i, auto cur) {
+      constexpr int kCur = decltype(cur)::value;
       const int t = t_first + i;
-      if (tile_active(t)) {
-        qk(i & 1);
-        softmax(t);
-        pv(i & 1);
+      const bool more = i + 1 < ntiles;
+      if (more) {
+        load_tile(ent, kCur ^ 1);
+        fetch_entries(t + 2, ent);
       }
-      if (i + 1 < ntiles) {
-        store_tile(t + 1, (i + 1) & 1, ka_, va_);
-        if (i + 3 < ntiles) {
-          load_tile(ent, ka_, va_);
-          fetch_entries(t + 4, ent);
-        }
+      if (tile_active(t)) {
+        qk(kCur);
+        softmax(t);
+        pv(kCur);
+      }
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(0);
+        zero_tail(t + 1, kCur ^ 1);
       }
       __syncthreads();
     };
     for (int i = 0; i < ntiles; i += 2) {
-      step(i, kr, vr);                         // stores tile i+1 (set A)
+      step(i, std::integral_constant<int, 0>());
       if (i + 1 >= ntiles) break;
-      step(i + 1, kr2, vr2);                   // stores tile i+2 (set B)
+      step(i + 1, std::integral_constant<int, 1>());
     }
   }
 
