@@ -41,7 +41,7 @@ def _values(rng, shape, dtype):
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(32))
 def test_decode_random_shapes(seed):
     rng = np.random.default_rng(5000 + seed)
     dtype = "f32" if seed % 4 == 0 else "bf16"
@@ -66,7 +66,7 @@ def test_decode_random_shapes(seed):
     compare(out, ref, dtype)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(32))
 def test_extend_random_shapes(seed):
     rng = np.random.default_rng(6000 + seed)
     BS = int(rng.choice([16, 32]))
