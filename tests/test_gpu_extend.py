@@ -249,14 +249,20 @@ def test_extend_long_context_split_sampled():
     log(f"  max-abs {worst:.3e} row max-rel {worst_rel:.3e}")
 
 
-def test_extend_and_block_move_replay_inside_a_captured_graph():
-    """Slot write, extend and a device-to-pinned-host block move captured in
-    one HIP graph, replayed several times with eager work in between; every
-    replay matches the eager result bit for bit."""
+@pytest.mark.parametrize("part_tokens", [0, 64])
+def test_extend_and_block_move_replay_inside_a_captured_graph(part_tokens):
+    """Slot write, extend (unsplit, or split with its merge kernel and a
+    caller-provided workspace) and a device-to-pinned-host block move
+    captured in one HIP graph, replayed several times with eager work in
+    between; every replay matches the eager result bit for bit."""
     cfg = EXTEND_CONFIGS["x5_extend_mha_bf16"]
     w = generate_extend_host(cfg)
     d = _upload(w)
     out = torch.empty_like(d["q"])
+    need = pkv.extend_workspace_size(d["k_cache"], cfg.num_seqs, w.num_tokens, cfg.q_heads,
+                                     w.max_query_len, w.max_seq_len, part_tokens)
+    assert (need > 0) == (part_tokens > 0)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     NB = w.layout.num_blocks
     host_k = torch.zeros((8,) + tuple(d["k_cache"].shape[1:]), dtype=torch.bfloat16).pin_memory()
     host_v = torch.zeros_like(host_k).pin_memory()
@@ -267,7 +273,7 @@ def test_extend_and_block_move_replay_inside_a_captured_graph():
         pkv.paged_kv_write(d["new_k"], d["new_v"], d["slot_mapping"], d["k_cache"], d["v_cache"])
         pkv.paged_attn_extend(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
                               d["seq_lens"], d["query_start"], cfg.scale, w.max_query_len,
-                              w.max_seq_len, out=out)
+                              w.max_seq_len, out=out, part_tokens=part_tokens, workspace=ws)
         pkv.paged_block_move(pairs, d["k_cache"], d["v_cache"], host_k, host_v)
 
     step()
