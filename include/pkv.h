@@ -1,6 +1,6 @@
 /*
- * pkv.h - C ABI of libpkv: paged KV-cache decode attention for AMD Instinct
- * MI355X (gfx950).
+ * pkv.h - C ABI of libpkv: paged KV-cache attention (decode and multi-token
+ * extend) and its block operations for AMD Instinct MI355X (gfx950).
  *
  * The cache of one attention layer is split into fixed-size physical blocks,
  * each holding the keys (one array) or values (a second array) of
@@ -40,7 +40,8 @@
  *           q, out: [num_seqs, q_heads, head_dim] of the cache dtype for
  *                   decode; [num_tokens, q_heads, head_dim] for extend.
  *           bf16 is IEEE binary32's upper 16 bits (bfloat16).
- *           Cache, q, k, v and out pointers must be 16-byte aligned.
+ *           Cache, q, k, v, out and workspace pointers must be 16-byte
+ *           aligned.
  * Errors.   Arguments are checked on the host before anything is launched;
  *           on any failure nothing is launched and a non-zero pkv_status is
  *           returned, with a message from pkv_last_error().  PKV_ERR_HIP
