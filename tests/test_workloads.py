@@ -92,7 +92,26 @@ def test_cow_layout_pairs_and_tables():
 
 # --- prefill / extend batches ------------------------------------------------------
 
-from workloads import EXTEND_CONFIGS, extend_slots, generate_extend_host  # noqa: E402
+from workloads import (EXTEND_CONFIGS, extend_layout, extend_slots,  # noqa: E402
+                       generate_extend_host)
+
+
+@pytest.mark.parametrize("name", sorted(EXTEND_CONFIGS))
+def test_extend_layouts_fit_their_tables(name):
+    """Every prefill / extend batch's lengths respect its ranges, fit its
+    table width and get distinct in-pool blocks (layout only, no values)."""
+    cfg = EXTEND_CONFIGS[name]
+    ctx, new, lay = extend_layout(cfg, np.random.default_rng(cfg.seed))
+    if not cfg.ctx_lens:
+        assert ctx.min() >= cfg.ctx_range[0] and ctx.max() <= cfg.ctx_range[1]
+    if not cfg.new_lens:
+        assert new.min() >= cfg.new_range[0] and new.max() <= cfg.new_range[1]
+    assert np.array_equal(lay.seq_lens, ctx + new)
+    assert lay.seq_lens.max() <= cfg.max_len
+    assert lay.block_table.shape == (cfg.num_seqs, cfg.table_width)
+    used = lay.block_table[lay.block_table >= 0]
+    assert used.size == int((-(-lay.seq_lens // cfg.block_size)).sum())
+    assert np.unique(used).size == used.size and used.max() < lay.num_blocks
 
 
 @pytest.mark.parametrize("name", ["x1_extend_tiny_bf16", "x4_extend_g8_bs32_bf16",
