@@ -594,7 +594,7 @@ def extend_bench(args):
         "extend_timing_ms": percentiles(attn_list),
         "roofline": {
             "bound": "mfma",
-            "kernel": "paged_attn_extend",
+            "kernel": "paged_attn_extend" + (" (partition + merge)" if num_parts > 1 else ""),
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
