@@ -69,6 +69,35 @@ MUTATIONS = {
     "block copy skips V": (
         "cache_ops.py", "    k_cache[dst] = k_src\n    v_cache[dst] = v_src",
         "    k_cache[dst] = k_src", "test_oracle_bf16_and_ops.py"),
+    "blocks_for rounds down": (
+        "block_manager.py", "    return -(-length // block_size)", "    return length // block_size",
+        "test_oracle_block_manager.py"),
+    "freed block never returns to the pool": (
+        "block_manager.py", "            self.fill[b] = 0\n            self.free.append(b)",
+        "            self.fill[b] = 0", "test_oracle_block_manager.py"),
+    "shared block written without a copy": (
+        "block_manager.py", "                if self.refcount[b] > 1:",
+        "                if self.refcount[b] > 99:", "test_oracle_block_manager.py"),
+    "copy-on-write keeps the old reference": (
+        "block_manager.py",
+        "                    self.fill[nb] = self.fill[b]\n                    self.refcount[b] -= 1",
+        "                    self.fill[nb] = self.fill[b]", "test_oracle_block_manager.py"),
+    "fork does not share": (
+        "block_manager.py", "        for b in self.tables[child]:\n            self.refcount[b] += 1",
+        "        self.tables[child] = [self._take() for _ in self.tables[child]]",
+        "test_oracle_block_manager.py"),
+    "prefix hit does not take a reference": (
+        "block_manager.py", "            self.refcount[b] += 1\n            self.tables[seq].append(b)",
+        "            self.tables[seq].append(b)", "test_oracle_block_manager.py"),
+    "prefix entry outlives its block": (
+        "block_manager.py", "            if key is not None:\n                del self.cache[key]",
+        "            pass", "test_oracle_block_manager.py"),
+    "swap-in fills every block": (
+        "block_manager.py", "            self.fill[b] = min(BS, length - j * BS)",
+        "            self.fill[b] = BS", "test_oracle_block_manager.py"),
+    "waste counts the used slots": (
+        "block_manager.py", '"unused_slots": slots - used,', '"unused_slots": used,',
+        "test_oracle_block_manager.py"),
     "bf16 widening shift wrong": (
         "bf16.py", "        word = a.astype(np.uint32) << np.uint32(16)",
         "        word = a.astype(np.uint32) << np.uint32(15)", "test_oracle_bf16_and_ops.py"),
