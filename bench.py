@@ -24,6 +24,7 @@ against the bf16 matrix-core peak.
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -46,6 +47,9 @@ def parse_args(argv=None):
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--part-tokens", type=int, default=None,
                    help="split-K partition length (default: the workload's, else the library's)")
+    p.add_argument("--block-size", type=int, default=None,
+                   help="run the batch with this block size instead of its own (same "
+                        "lengths and values recipe, new placement)")
     p.add_argument("--cpu-sample", type=int, default=256,
                    help="sequences the oracle computes for the CPU baseline (0 skips it)")
     p.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
@@ -466,6 +470,8 @@ def extend_bench(args):
 
     ensure_built()
     cfg = EXTEND_CONFIGS[args.workload]
+    if args.block_size is not None:
+        cfg = dataclasses.replace(cfg, block_size=args.block_size)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
@@ -602,7 +608,8 @@ def extend_bench(args):
             "flops_per_launch": flops,
             "kv_bytes_per_launch": kv_bytes + io_bytes,
             # the summaries were taken at the library's own partition choice
-            "traffic": profiled_traffic(cfg.name) if not args.part_tokens else None,
+            "traffic": (profiled_traffic(cfg.name)
+                        if not args.part_tokens and args.block_size is None else None),
         },
         "cpu_baseline": cpu,
     }
@@ -638,6 +645,8 @@ def main(argv=None):
     cfg = get_config(args.workload)
     if args.part_tokens is not None:
         cfg = scaled(cfg, part_tokens=args.part_tokens)
+    if args.block_size is not None:
+        cfg = scaled(cfg, block_size=args.block_size)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
@@ -761,7 +770,9 @@ def main(argv=None):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "bytes_per_launch": roof_bytes,
             # the summaries were taken at each batch's own partition length
-            "traffic": profiled_traffic(cfg.name) if args.part_tokens is None else None,
+            # and block size
+            "traffic": (profiled_traffic(cfg.name)
+                        if args.part_tokens is None and args.block_size is None else None),
         },
         "cpu_baseline": cpu,
         "ops": ops,

@@ -38,6 +38,11 @@ def test_decode_step_bytes_follow_the_formula():
     assert b["shared_repeat"] == 0
 
 
+def test_block_size_override_is_optional():
+    assert bench.parse_args([]).block_size is None
+    assert bench.parse_args(["--block-size", "32"]).block_size == 32
+
+
 def test_percentiles():
     p = bench.percentiles([float(x) for x in range(1, 102)])
     assert p == {"p10": 11.0, "p50": 51.0, "p90": 91.0}
