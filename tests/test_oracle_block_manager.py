@@ -109,6 +109,24 @@ def test_out_of_blocks():
         bm.append(0, 1)
 
 
+def test_short_requests_pay_a_whole_block_each():
+    """[GL] "What people get wrong": capacity is counted in whole pages, so
+    thousands of short requests still hold one block each."""
+    BS, n = 16, 4096
+    bm = BlockManager(n, BS)
+    for s in range(n):
+        bm.add(s)
+        bm.append(s, 1 + s % 4)           # 1..4 tokens, 2.5 on average
+    st = bm.stats()
+    assert st["allocated_blocks"] == n and st["free_blocks"] == 0
+    assert st["used_slots"] == 10_240     # 1024 requests of each length 1..4
+    assert st["unused_slots"] == n * BS - 10_240
+    assert st["waste_fraction"] == 1 - 10_240 / (n * BS)   # 84.4%
+    bm.add(n)
+    with pytest.raises(OutOfBlocks):
+        bm.append(n, 1)
+
+
 def test_c4_layout_replays_through_the_block_manager():
     """Fork 128 sequences from a 1024-token prefix, then append each suffix."""
     cfg = get_config("c4_prefix_bf16")
