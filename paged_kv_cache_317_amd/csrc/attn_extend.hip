@@ -47,10 +47,10 @@
 //                 bf16), V^T comes from the V tile through
 //                 ds_read_b64_tr_b16 transpose reads, shared by both groups.
 // Loads: the next tile's K and V rows go straight from global memory into
-// the other LDS buffer (global_load_lds_dwordx4, 16 bytes per lane, 1 KB
+// the other LDS buffer (buffer_load_dwordx4 ... lds, 16 bytes per lane, 1 KB
 // per wave instruction) while the current tile computes; one barrier per
 // tile.  The LDS rows are unpadded and their 16-byte chunks XOR-swizzled by
-// row, which keeps both operand reads free of bank conflicts.
+// row, which spreads both operand reads over the LDS banks.
 #include "device_common.hpp"
 #include "extend.hpp"
 
@@ -72,6 +72,9 @@ constexpr int kWaveCols = 16 * kGroups;
 constexpr int kRow = kD * 2;             // LDS row of a K or V tile (bytes, unpadded)
 constexpr int kTile = kKeys * kRow;
 constexpr float kLazyLog2 = 8.f;         // running-max slack before O is rescaled
+// Fourth word of a buffer resource for raw loads: 32-bit data format, no
+// swizzle, no stride (num_records then counts bytes).
+constexpr int kBufferWord3 = 0x00020000;
 static_assert(kExtendCols == kWaves * 16 * kGroups, "kWaves waves of kGroups 16-column groups");
 static_assert(kKeys % kStep == 0, "whole rows per thread");
 static_assert(kStep % 16 == 0, "a load pass keeps every row's index mod 16");
@@ -196,6 +199,10 @@ void extend_kernel(ExtendArgs a) {
   // global memory into LDS; lane l of wave w writes the l-th 16 bytes of
   // rows 4 w .. 4 w + 3 (+ kStep i), i.e. row lrow = l / 16 + 4 w, physical
   // chunk lchunk = l % 16, so it fetches the logical chunk lchunk ^ swizzle.
+  // The loads are buffer loads through a resource spanning the one block
+  // they read: with the flat-encoded global form the compiler cannot keep
+  // partial LDS wait counts and drains every operand read (measured 3-6%
+  // slower).
   const int lchunk = threadIdx.x & 15;
   const int lrow = threadIdx.x >> 4;
   const uint32_t lane_off =
@@ -221,12 +228,16 @@ void extend_kernel(ExtendArgs a) {
       const uint64_t base = (uint64_t)phys * a.block_bytes;
       const uint32_t off = (uint32_t)(((lrow + kStep * i) % BS) * a.row_bytes) + lane_off;
       const int lds_row = uniform_int(wave_row + kStep * i);
-      __builtin_amdgcn_global_load_lds(
-          kcache + base + off,
-          (__attribute__((address_space(3))) void*)(s_k[buf] + lds_row * kRow), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          vcache + base + off,
-          (__attribute__((address_space(3))) void*)(s_v[buf] + lds_row * kRow), 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(kcache + base), 0, (int)a.block_bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(vcache + base), 0, (int)a.block_bytes, kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(s_k[buf] + lds_row * kRow), 16, (int)off,
+          0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(s_v[buf] + lds_row * kRow), 16, (int)off,
+          0, 0, 0);
     }
   };
   // Once this lane's loads of `tile` have landed: the rows it loaded at or
