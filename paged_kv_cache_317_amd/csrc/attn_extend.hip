@@ -228,16 +228,20 @@ void extend_kernel(ExtendArgs a) {
       const uint64_t base = (uint64_t)phys * a.block_bytes;
       const uint32_t off = (uint32_t)(((lrow + kStep * i) % BS) * a.row_bytes) + lane_off;
       const int lds_row = uniform_int(wave_row + kStep * i);
+      // Sizes and offsets are unsigned 32-bit in the hardware; the builtins
+      // take them as int, bit for bit.
+      const int nrec = __builtin_bit_cast(int, a.block_bytes);
+      const int voff = __builtin_bit_cast(int, off);
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char*>(kcache + base), 0, (int)a.block_bytes, kBufferWord3);
+          const_cast<char*>(kcache + base), 0, nrec, kBufferWord3);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char*>(vcache + base), 0, (int)a.block_bytes, kBufferWord3);
+          const_cast<char*>(vcache + base), 0, nrec, kBufferWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(s_k[buf] + lds_row * kRow), 16, (int)off,
-          0, 0, 0);
+          rk, (__attribute__((address_space(3))) void*)(s_k[buf] + lds_row * kRow), 16, voff, 0,
+          0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(s_v[buf] + lds_row * kRow), 16, (int)off,
-          0, 0, 0);
+          rv, (__attribute__((address_space(3))) void*)(s_v[buf] + lds_row * kRow), 16, voff, 0,
+          0, 0);
     }
   };
   // Once this lane's loads of `tile` have landed: the rows it loaded at or
