@@ -603,6 +603,86 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_reduce_kernel(DecodeA
   }
 }
 
+// Merge for calls with few partitions per sequence (at most NP): one wave
+// per (sequence, query head) row, four rows per workgroup.  Each lane loads
+// the row's (m, l) of every partition and its own D / 64 output elements of
+// each, all before any arithmetic, so the merge costs one round trip to
+// memory; the max and the weighted sums then run in registers in partition
+// order (fixed, so the result does not depend on timing).  Slots past the
+// row's last partition re-read that partition (written by the partition
+// kernel, so finite) and carry no weight.
+template <typename T, int D, int BS, int NP>
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_few_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const int lane = threadIdx.x & 63;
+  const int orow = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (orow >= a.num_seqs * a.q_heads) return;
+  const int s = orow / a.q_heads;
+  const int h = orow - s * a.q_heads;
+  const int L = clamp_len(a, s, BS);
+  const int P = (L + a.part_tokens - 1) / a.part_tokens;
+  const int64_t stride = a.q_heads;
+  const int64_t row0 = (int64_t)s * a.num_parts * a.q_heads + h;
+  const float* ml = a.part_ml + row0 * 2;
+  const int64_t o_off = row0 * D + lane * PER;
+  const float* po32 = reinterpret_cast<const float*>(a.part_o) + o_off;
+  const uint16_t* po16 = reinterpret_cast<const uint16_t*>(a.part_o) + o_off;
+
+  if (P == 0) {                       // empty sequence: zero row, nothing to read
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if constexpr (kBf16)
+        reinterpret_cast<__bf16*>(a.out)[(int64_t)orow * D + lane * PER + e] = (__bf16)0.f;
+      else
+        reinterpret_cast<float*>(a.out)[(int64_t)orow * D + lane * PER + e] = 0.f;
+    }
+    return;
+  }
+  float mv[NP], lv[NP], ov[NP][PER];
+  const int plast = P - 1;
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int p = min(u, plast);
+    mv[u] = ml[2 * p * stride];
+    lv[u] = ml[2 * p * stride + 1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      ov[u][e] = kBf16 ? __uint_as_float((uint32_t)po16[(int64_t)p * stride * D + e] << 16)
+                       : po32[(int64_t)p * stride * D + e];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NP; ++u) M = u < P ? fmaxf(M, mv[u]) : M;
+  float lsum = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    // A partition with no tokens (m = -inf), or past the row's last one,
+    // carries no weight.
+    const bool live = u < P && mv[u] != -INFINITY;
+    const float w = live ? __builtin_amdgcn_exp2f(mv[u] - M) : 0.f;
+    const float wl = w * lv[u];
+    lsum += wl;
+    const float wo = kBf16 ? wl : w;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wo, ov[u][e], acc[e]);
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if constexpr (kBf16) {
+    static_assert(PER == 2, "bf16 merge writes two elements per lane");
+    __bf16* out = reinterpret_cast<__bf16*>(a.out) + (int64_t)orow * D + lane * PER;
+    out[0] = (__bf16)(acc[0] * inv);
+    out[1] = (__bf16)(acc[1] * inv);
+  } else {
+    float* out = reinterpret_cast<float*>(a.out) + (int64_t)orow * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = acc[e] * inv;
+  }
+}
+
 template <typename T, int D, int BS, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int groups = a.kv_heads / a.heads_per_wg;
@@ -612,8 +692,20 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
                      dim3(64 * a.heads_per_wg), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_parts == 1) return err;
-  hipLaunchKernelGGL((decode_reduce_kernel<T, D, BS>), dim3((unsigned)(a.num_seqs * a.q_heads)),
-                     dim3(64 * kMergeWaves), 0, stream, a);
+  const int64_t rows = (int64_t)a.num_seqs * a.q_heads;
+  const dim3 few_grid((unsigned)((rows + kMergeWaves - 1) / kMergeWaves));
+  const dim3 threads(64 * kMergeWaves);
+  if (a.num_parts <= 2)
+    hipLaunchKernelGGL((decode_merge_few_kernel<T, D, BS, 2>), few_grid, threads, 0, stream, a);
+  else if (a.num_parts <= 4)
+    hipLaunchKernelGGL((decode_merge_few_kernel<T, D, BS, 4>), few_grid, threads, 0, stream, a);
+  else if (a.num_parts <= 8)
+    hipLaunchKernelGGL((decode_merge_few_kernel<T, D, BS, 8>), few_grid, threads, 0, stream, a);
+  else if (a.num_parts <= 16)
+    hipLaunchKernelGGL((decode_merge_few_kernel<T, D, BS, 16>), few_grid, threads, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, BS>), dim3((unsigned)rows), threads, 0, stream,
+                       a);
   return hipGetLastError();
 }
 
