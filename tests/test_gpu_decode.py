@@ -209,6 +209,33 @@ def test_edge_lengths(lens):
             assert torch.count_nonzero(got[s]) == 0
 
 
+@pytest.mark.parametrize("dtype_case", ["bf16", "f32"])
+@pytest.mark.parametrize("nparts", [2, 3, 4, 5, 8, 9, 16, 17])
+def test_partition_counts_across_both_merges(dtype_case, nparts):
+    """Split calls with 2 .. 17 partitions per sequence: up to 16 take the
+    one-wave-per-row merge, more the four-wave merge.  The batch holds an
+    empty sequence, sequences shorter than one partition, one ending one
+    token into a partition and one filling every partition."""
+    if dtype_case == "bf16":
+        base = get_config("c3_gqa4k_bf16")
+        part = 16
+    else:
+        base = scaled(get_config("c1_tiny_f32"), q_heads=8, kv_heads=2, block_size=32,
+                      pool_blocks=0)
+        part = 32
+    top = nparts * part
+    lens = np.array([0, 1, part - 1, part + 1, top - part + 1, top], dtype=np.int32)
+    cfg = scaled(base, num_seqs=len(lens), seq_lens=tuple(int(max(l, 1)) for l in lens),
+                 max_len=top)
+    w = generate_host(cfg)
+    log(f"merge {dtype_case}: parts={nparts} part_tokens={part} lens={list(lens)}")
+    d = upload(w)
+    assert pkv.decode_partition_tokens(d["k_cache"], cfg.num_seqs, cfg.q_heads, top, part) == part
+    got = _decode(d, w, part_tokens=part, seq_lens=to_device(lens, None), max_seq_len=top)
+    compare(got, oracle_decode(w, seq_lens=lens), cfg.dtype)
+    assert torch.count_nonzero(got[0]) == 0
+
+
 def test_max_seq_len_cuts_sequences():
     """A sequence longer than max_seq_len is attended up to max_seq_len."""
     w = _case("c3s")
