@@ -47,7 +47,7 @@
 // the output normalised by the sum and rounded to bf16 for bf16 caches
 // (unnormalised fp32 for f32 caches) -- into the workspace, ordered
 // [sequence, partition, head] so that a wave's heads are adjacent and leave
-// through its LDS tile in whole runs.  A second kernel merges the
+// through its LDS tile in whole runs (device-scope stores).  A second kernel merges the
 // partitions with the log-sum-exp rule in a fixed order (deterministic, no
 // atomics).  A workgroup may walk several consecutive partitions (a build
 // option), emitting each one's state at its last tile.
@@ -65,6 +65,11 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kTile = 16;
+// Fourth word of a buffer resource for raw accesses: 32-bit data format, no
+// swizzle, no stride (num_records then counts bytes).
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer store: the sc1 bit (device scope).
+constexpr int kStoreDeviceScope = 16;
 // Kv heads (one wave each) a decode workgroup can hold.
 #ifndef PKV_DECODE_MAX_WAVES
 #define PKV_DECODE_MAX_WAVES 4
@@ -390,7 +395,7 @@ void decode_partition_kernel(DecodeArgs a) {
       // bf16 caches: the partition's output is stored normalised (o / l) in
       // bf16, next to its max and sum in fp32.  It goes through this wave's
       // V tile (free between tiles) so that the workspace is written in
-      // whole runs, 16 bytes per lane, with non-temporal stores.
+      // whole runs, 16 bytes per lane.
       char* st = vt;
       if (lc < G) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -405,12 +410,18 @@ void decode_partition_kernel(DecodeArgs a) {
           *reinterpret_cast<float2*>(a.part_ml + 2 * (row0 + lc)) = float2{m_run, l_tot};
       }
       __builtin_amdgcn_wave_barrier();
+      // Buffer stores with device scope (the sc1 cache-policy bit): of the
+      // store policies measured on the long-context split (regular,
+      // non-temporal, sc0, sc1, both scopes, with and without nt) this one
+      // disturbed the read stream least.
       __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + row0 * D;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(po, 0, G * D * 2, kBufferWord3);
 #pragma unroll
       for (int idx = 8 * lane; idx < G * D; idx += 8 * kWave)
-        __builtin_nontemporal_store(
+        __builtin_amdgcn_raw_buffer_store_b128(
             *reinterpret_cast<const u32x4_t*>(st + (idx / D) * kStageRowBytes + 2 * (idx % D)),
-            reinterpret_cast<u32x4_t*>(po + idx));
+            rs, idx * 2, 0, kStoreDeviceScope);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int dt = 0; dt < kDimTiles; ++dt) ot[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
