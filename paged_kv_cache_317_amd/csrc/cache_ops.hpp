@@ -30,6 +30,7 @@ struct BlockMoveArgs {
   int64_t src_blocks;
   int64_t dst_blocks;
   int64_t block_bytes;   // block_size * kv_heads * head_dim * element bytes
+  bool streaming;        // both pools on the device: non-temporal loads and stores
 };
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);

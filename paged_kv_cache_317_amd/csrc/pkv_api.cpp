@@ -458,6 +458,7 @@ PKV_EXPORT pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pai
   a.dst_k = k_cache;
   a.dst_v = v_cache;
   a.src_blocks = a.dst_blocks = cache->num_blocks;
+  a.streaming = true;
   a.block_bytes = (int64_t)cache->block_size * cache->kv_heads * cache->head_dim *
                   elem_bytes(cache->dtype);
   const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
@@ -533,5 +534,6 @@ PKV_EXPORT pkv_status pkv_paged_block_move(const int64_t* pairs, int32_t num_pai
   const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
   if ((int64_t)num_pairs * 2 * chunks > INT32_MAX)
     return fail(PKV_ERR_SHAPE, "too many pairs for one launch");
+  a.streaming = false;
   return from_hip(pkv::launch_block_move(a, (hipStream_t)stream), "paged_block_move launch");
 }
