@@ -157,10 +157,38 @@ def _pinned_pool(shape, dtype):
     return torch.zeros(shape, dtype=dtype).pin_memory()
 
 
+# Block shapes around the copy kernel's 32 KiB chunk: 8 KiB (f32, 2 kv
+# heads, head_dim 64: one partial chunk) and 48 KiB (bf16, 12 kv heads: one
+# whole chunk and a half).
+PARTIAL_CHUNK_SHAPES = [
+    ("c1_tiny_f32", dict(q_heads=2, kv_heads=2)),
+    ("c3_gqa4k_bf16", dict(num_seqs=6, q_heads=12, kv_heads=12, len_range=(30, 200),
+                           max_len=256)),
+]
+
+
+@pytest.mark.parametrize("name,kw", PARTIAL_CHUNK_SHAPES)
+def test_block_copy_partial_chunks_bit_exact(name, kw):
+    """Blocks that are not a whole number of the kernel's 32 KiB chunks."""
+    cfg = scaled(get_config(name), **kw)
+    w = generate_host(cfg)
+    NB = w.layout.num_blocks
+    rng = np.random.default_rng(5)
+    ids = rng.choice(NB, size=12, replace=False)
+    pairs = np.stack([ids[:6], ids[6:]], 1).astype(np.int64)
+    log(f"block_copy {name} {kw} block_bytes={w.k_cache[0].nbytes} pairs={len(pairs)}")
+    d = upload(w)
+    pkv.paged_block_copy(to_device(pairs, None), d["k_cache"], d["v_cache"])
+    torch.cuda.synchronize()
+    rk, rv = oracle.block_copy(w.k_cache, w.v_cache, pairs)
+    assert np.array_equal(to_host(d["k_cache"], cfg.dtype), rk)
+    assert np.array_equal(to_host(d["v_cache"], cfg.dtype), rv)
+
+
 @pytest.mark.parametrize("name,kw", [
     ("c1_tiny_f32", {}),
     ("c3_gqa4k_bf16", dict(num_seqs=6, len_range=(30, 200), max_len=256)),
-])
+] + PARTIAL_CHUNK_SHAPES)
 def test_block_move_device_host_device_bit_exact(name, kw):
     cfg = scaled(get_config(name), **kw)
     w = generate_host(cfg)
