@@ -663,6 +663,7 @@ def main(argv=None):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     part = pkv.decode_partition_tokens(w.k_cache, cfg.num_seqs, cfg.q_heads, max_len,
                                        cfg.part_tokens)
+    runs = pkv.decode_runs(w.k_cache, cfg.num_seqs, cfg.q_heads, max_len, cfg.part_tokens)
 
     def write():
         pkv.paged_kv_write(w.new_k, w.new_v, w.slot_mapping, w.k_cache, w.v_cache)
@@ -755,6 +756,7 @@ def main(argv=None):
             "seq_lens": [int(lay.seq_lens.min()), int(lay.seq_lens.max())],
             "pool_blocks": lay.num_blocks,
             "part_tokens": part,
+            "runs": runs,
             "step": "paged_kv_write (one token per sequence) + paged_attn_decode",
         },
         "seqs_per_s": round(cfg.num_seqs / (step_ms * 1e-3), 1),
@@ -763,7 +765,7 @@ def main(argv=None):
         "decode_timing": decode_stats,
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attn_decode" + (" (partition + merge)" if part < max_len else ""),
+            "kernel": "paged_attn_decode" + (" (stream + merge)" if runs > 1 else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

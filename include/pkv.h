@@ -50,10 +50,10 @@
  * Device-side safety.  Values read from device memory (slots, table entries,
  *           copy pairs) cannot be checked on the host.  Kernels never touch
  *           memory outside the pool for an id outside it: such a slot or copy
- *           pair is skipped, decode stops reading a sequence's partition at
- *           such a table entry (the output for that sequence is then
- *           unspecified) and extend stops the sequence there.  That is a
- *           guard, not a contract: callers must pass valid ids.
+ *           pair is skipped, decode leaves the positions of such a table
+ *           entry's block out of the sequence (the same in every split), and
+ *           extend stops the sequence at it.  That is a guard, not a
+ *           contract: callers must pass valid ids.
  * Threads.  The library keeps no state between calls apart from the
  *           thread-local last-error message, so calls from several host
  *           threads are safe; ordering between them is the streams'.
@@ -127,25 +127,42 @@ pkv_status pkv_paged_kv_write(const void* k, const void* v,
  *   q            device, [num_seqs, q_heads, head_dim]
  *   k_cache, v_cache  device, read only
  *   block_table  device, int32 [num_seqs, table_width]; entries at or past
- *                ceil(L / block_size) are never read
+ *                ceil(L / block_size) are never read.  Sequences may share
+ *                physical blocks ("Sharing blocks between sequences"): when
+ *                consecutive sequences (16 / G of them for bf16 caches) hold
+ *                the same leading blocks, those blocks are read once for all
+ *                of them.  An entry outside [0, num_blocks) is invalid input;
+ *                the kernels never read outside the pool for it, and the
+ *                positions of that block are left out of the sequence's
+ *                attention (in every split; other sequences are unaffected).
  *   seq_lens     device, int32 [num_seqs]
  *   max_seq_len  host-side bound on every seq_lens[s] (sizes the grid without
  *                reading device memory); a sequence is cut to
  *                min(seq_lens[s], max_seq_len, table_width * block_size)
  *   scale        softmax scale, typically 1/sqrt(head_dim)
  *   out          device, [num_seqs, q_heads, head_dim], written
- *   part_tokens  split-K partition length in tokens (rounded up to a
- *                multiple of block_size), or 0 to let the library choose;
- *                pkv_decode_partition_tokens() reports the choice
+ *   part_tokens  partition length in tokens (rounded up to a multiple of
+ *                16, at most 8192), or 0 for 16.  The call's work -- every
+ *                sequence's positions, sequence after sequence -- is cut
+ *                into partitions of this length (a sequence's last one may be
+ *                shorter), and the partitions into pkv_decode_runs() equal
+ *                runs, one workgroup per run and group of up to four kv
+ *                heads; a run carries its softmax state across the
+ *                partitions of one sequence and may span several sequences.
+ *                pkv_decode_partition_tokens() reports the length used.
  *   workspace    device scratch of at least pkv_decode_workspace_size()
- *                bytes when the call splits (more than one partition);
- *                may be NULL when that size is 0.  Contents need no
- *                initialisation and are left undefined.  It holds each
- *                partition's max and sum (fp32) and output (bf16 caches:
- *                normalised, in bf16; f32 caches: fp32), merged by a second
- *                kernel in a fixed order.
+ *                bytes when the call has more than one run; may be NULL when
+ *                that size is 0.  Contents need no initialisation and are
+ *                left undefined.  It holds the plan of the call and, for each
+ *                sequence more than one run contributes to, each run's max,
+ *                sum and unnormalised output (fp32), merged by a second
+ *                kernel in run order.
+ * The result does not depend on where the blocks sit in the pool; it can
+ * differ in the last bits between batches that split a sequence's work
+ * differently (other lengths, other sharing), within the fp32 accumulation.
  * Supported: f32 with head_dim 64, bf16 with head_dim 128; block_size 16 or
- * 32; G in {1, 2, 4, 8}.
+ * 32; G in {1, 2, 4, 8}; num_seqs up to about 14000 (PKV_ERR_UNSUPPORTED
+ * beyond).
  */
 pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,
                                  const void* v_cache,
@@ -232,17 +249,23 @@ size_t pkv_extend_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
                                  int32_t part_tokens);
 
 /*
- * Partition length (tokens) pkv_paged_attn_decode uses for these arguments;
- * the call is split when it is below max_seq_len.  Returns 0 on invalid
- * arguments (see pkv_last_error()).
+ * Partition length (tokens) pkv_paged_attn_decode uses for these arguments.
+ * Returns 0 on invalid arguments (see pkv_last_error()).
  */
 int32_t pkv_decode_partition_tokens(const pkv_cache_desc* cache,
                                     int32_t num_seqs, int32_t q_heads,
                                     int32_t max_seq_len, int32_t part_tokens);
 
 /*
+ * Runs pkv_paged_attn_decode cuts the work of these arguments into (1: one
+ * kernel, no workspace).  Returns 0 on invalid arguments.
+ */
+int32_t pkv_decode_runs(const pkv_cache_desc* cache, int32_t num_seqs, int32_t q_heads,
+                        int32_t max_seq_len, int32_t part_tokens);
+
+/*
  * Workspace bytes pkv_paged_attn_decode needs for these arguments (0 when it
- * does not split).  Returns 0 on invalid arguments as well; check
+ * has one run).  Returns 0 on invalid arguments as well; check
  * pkv_last_error() when in doubt.
  */
 size_t pkv_decode_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,

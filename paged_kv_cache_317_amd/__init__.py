@@ -10,6 +10,7 @@ from ._lib import PkvError, lib, LIB_PATH
 from .ops import (
     cache_desc,
     decode_partition_tokens,
+    decode_runs,
     decode_workspace_size,
     extend_partition_tokens,
     extend_workspace_size,
@@ -26,6 +27,7 @@ __all__ = [
     "LIB_PATH",
     "cache_desc",
     "decode_partition_tokens",
+    "decode_runs",
     "decode_workspace_size",
     "extend_partition_tokens",
     "extend_workspace_size",

@@ -58,6 +58,7 @@ SIGNATURES = {
     "pkv_extend_workspace_size": (_sz, [_desc, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_partition_tokens": (_i32, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_decode_workspace_size": (_sz, [_desc, _i32, _i32, _i32, _i32]),
+    "pkv_decode_runs": (_i32, [_desc, _i32, _i32, _i32, _i32]),
     "pkv_paged_block_copy": (_i32, [_vp, _i32, _vp, _vp, _desc, _vp]),
     "pkv_paged_block_move": (_i32, [_vp, _i32, _vp, _vp, _desc, _vp, _vp, _desc, _vp]),
     "pkv_bm_create": (_i32, [_i32, _i32, _vp, _p(_vp)]),

@@ -21,15 +21,23 @@ namespace pkv {
 const char* last_error();
 }
 
-// Waves a split decode keeps when its workgroups walk several partitions
-// each (0: one partition per workgroup).
-#ifndef PKV_DECODE_WALK_WAVES
-#define PKV_DECODE_WALK_WAVES 0
-#endif
-
 // Kv heads (one wave each) per decode workgroup, when kv_heads allows it.
 #ifndef PKV_DECODE_HEADS_PER_WG
 #define PKV_DECODE_HEADS_PER_WG 4
+#endif
+
+// Waves a decode grid aims for: the work stream is cut into this many waves'
+// worth of runs (kv_heads waves per run).
+#ifndef PKV_DECODE_WAVE_TARGET
+#define PKV_DECODE_WAVE_TARGET 2048
+#endif
+
+// Work of a run on an odd XCD relative to one on an even XCD, in 1/1024.  On
+// the HBM-bound decode gather the odd XCDs of an MI355X take about 8% longer
+// per tile than the even ones (per-wave timing, several batches and boxes),
+// so equal runs leave the even XCDs idle at the end of the call.
+#ifndef PKV_DECODE_ODD_XCD_Q10
+#define PKV_DECODE_ODD_XCD_Q10 942
 #endif
 
 namespace pkv {
@@ -85,33 +93,28 @@ pkv_status check_cache(const pkv_cache_desc* c) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Split policy.  A partition is the unit of work of one wave per kv head; the
-// grid has num_seqs * kv_heads * partitions waves.  Without an explicit
-// request the call stays unsplit while that already gives enough waves to
-// fill the GPU (about 8 per CU on 256 CUs), and otherwise halves the
-// partition length (down to 512 tokens) until it does.  A partition never
-// exceeds the LDS table slice.
-constexpr int64_t kWaveTarget = 2048;
-constexpr int64_t kMinAutoPart = 512;
-
-int64_t part_tokens_for(const pkv_cache_desc& c, int64_t num_seqs, int64_t max_seq_len,
-                        int64_t requested) {
-  const int64_t BS = c.block_size;
-  const int64_t cap = (int64_t)pkv::kMaxPartBlocks * BS;
-  if (requested > 0) return requested >= cap ? cap : round_up(requested, BS);
-  int64_t pt = round_up(max_seq_len > 0 ? max_seq_len : 1, BS);
-  if (pt > cap) pt = cap;
-  const int64_t floor_pt = round_up(kMinAutoPart, BS);
-  auto waves = [&](int64_t p) { return num_seqs * c.kv_heads * ((max_seq_len + p - 1) / p); };
-  while (pt > floor_pt && waves(pt) < kWaveTarget) pt = round_up(pt / 2, BS);
-  return pt;
-}
+// Split policy.  The work stream (every sequence's tiles of 16 positions, in
+// partitions of part_tiles tiles) is cut into num_ranges equal runs, one
+// workgroup of up to four waves (kv heads) per run and kv-head group.  The
+// host sees only max_seq_len, so the run count comes from the largest
+// stream the call can have: enough runs for about kWaveTarget waves, no run
+// shorter than kMinRunTiles tiles on a full-length batch, and no run longer
+// than the kMaxRangeTiles tile slots a workgroup stages in LDS.  With one run
+// the call needs no workspace and no merge.
+constexpr int64_t kWaveTarget = PKV_DECODE_WAVE_TARGET;
+constexpr int64_t kMinRunTiles = 32;
 
 struct DecodePlan {
-  int64_t part_tokens = 0;
-  int64_t num_parts = 1;
+  int64_t part_tiles = 1;
+  int64_t num_ranges = 1;
+  int64_t odd_q10 = 1024;
+  int64_t lds = 0;
+  size_t plan_bytes = 0;    // workspace: stream plan (int32)
+  size_t ml_bytes = 0;      //            run states' (max, sum)
   size_t workspace = 0;
 };
+
+int64_t ceil_div64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_heads,
                        int32_t max_seq_len, int32_t part_tokens, DecodePlan* plan) {
@@ -127,14 +130,46 @@ pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_head
     return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for dtype %d, head_dim %d, block_size %d, "
                 "group %d (built: f32 head_dim 64, bf16 head_dim 128; block 16 or 32; group 1, "
                 "2, 4 or 8)", (int)c->dtype, (int)c->head_dim, (int)c->block_size, group);
-  plan->part_tokens = part_tokens_for(*c, num_seqs, max_seq_len, part_tokens);
-  plan->num_parts = max_seq_len > 0 ? (max_seq_len + plan->part_tokens - 1) / plan->part_tokens : 1;
-  plan->workspace = 0;
-  if (plan->num_parts > 1) {
-    const int64_t rows = (int64_t)num_seqs * q_heads * plan->num_parts;
-    // (max, sum) in fp32, then o in the cache's precision (bf16: normalised).
-    plan->workspace = (size_t)(round_up(2 * rows, 4) * sizeof(float) +
-                               rows * c->head_dim * elem_bytes(c->dtype));
+  const int64_t pt =
+      part_tokens > 0 ? std::min<int64_t>(ceil_div64(part_tokens, 16), pkv::kMaxRangeTiles) : 1;
+  // Tiles a member can own: its own tiles, or (block 32) the shared tiles of
+  // its group, one more at most.
+  const int64_t tmax = ceil_div64(max_seq_len, 16) + (c->block_size / 16 - 1);
+  const int64_t units_bound = (int64_t)num_seqs * ceil_div64(tmax, pt);
+  if (units_bound > INT32_MAX / 2)
+    return fail(PKV_ERR_SHAPE, "num_seqs * max_seq_len is too large for one decode call");
+  int64_t n = ceil_div64(kWaveTarget, c->kv_heads);
+  n = std::min(n, std::max<int64_t>(1, ceil_div64(units_bound, ceil_div64(kMinRunTiles, pt))));
+  n = std::max(n, ceil_div64(units_bound, pkv::kMaxRangeTiles / pt));
+  n = std::max<int64_t>(1, std::min(n, std::max<int64_t>(units_bound, 1)));
+  // From 8 runs on: a multiple of 8, each run on one XCD, odd XCDs' runs
+  // shorter; the longest (even) run still fits the staged tile slots.
+  int64_t odd_q10 = 1024;
+  if (n >= 8) {
+    n = round_up(n, 8);
+    odd_q10 = PKV_DECODE_ODD_XCD_Q10;
+    auto longest = [&](int64_t nn) {
+      const int64_t pairs_q10 = (nn / 2) * (1024 + odd_q10);
+      return ceil_div64(units_bound * 1024, pairs_q10);
+    };
+    while (longest(n) * pt > pkv::kMaxRangeTiles) n += 8;
+  }
+  plan->part_tiles = pt;
+  plan->num_ranges = n;
+  plan->odd_q10 = odd_q10;
+  plan->lds = pkv::decode_plan_lds_bytes(c->dtype, group, num_seqs);
+  if (plan->lds > pkv::decode_max_plan_lds_bytes())
+    return fail(PKV_ERR_UNSUPPORTED, "%d sequences exceed what one decode call plans in LDS "
+                "(split the batch)", (int)num_seqs);
+  plan->plan_bytes = plan->ml_bytes = plan->workspace = 0;
+  if (n > 1) {
+    const int64_t gs = pkv::decode_group_size(c->dtype, group);
+    const int64_t groups = ceil_div64(num_seqs, gs);
+    const int64_t slots = n + groups;
+    const int64_t rows = slots * c->kv_heads * gs * group;
+    plan->plan_bytes = (size_t)round_up(num_seqs + 1 + groups + 2, 4) * sizeof(int32_t);
+    plan->ml_bytes = (size_t)round_up(2 * rows, 4) * sizeof(float);
+    plan->workspace = plan->plan_bytes + plan->ml_bytes + (size_t)(rows * c->head_dim) * sizeof(float);
   }
   return PKV_OK;
 }
@@ -174,7 +209,15 @@ PKV_EXPORT int32_t pkv_decode_partition_tokens(const pkv_cache_desc* cache, int3
   DecodePlan plan;
   if (plan_decode(cache, num_seqs, q_heads, max_seq_len, part_tokens, &plan) != PKV_OK) return 0;
   ok();
-  return (int32_t)plan.part_tokens;
+  return (int32_t)(plan.part_tiles * 16);
+}
+
+PKV_EXPORT int32_t pkv_decode_runs(const pkv_cache_desc* cache, int32_t num_seqs,
+                                   int32_t q_heads, int32_t max_seq_len, int32_t part_tokens) {
+  DecodePlan plan;
+  if (plan_decode(cache, num_seqs, q_heads, max_seq_len, part_tokens, &plan) != PKV_OK) return 0;
+  ok();
+  return (int32_t)plan.num_ranges;
 }
 
 PKV_EXPORT size_t pkv_decode_workspace_size(const pkv_cache_desc* cache, int32_t num_seqs,
@@ -204,14 +247,13 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
   if (plan.workspace > 0) {
-    if (!workspace) return fail(PKV_ERR_WORKSPACE, "this call splits into %lld partitions and needs "
-                                "a %zu-byte workspace", (long long)plan.num_parts, plan.workspace);
+    if (!workspace) return fail(PKV_ERR_WORKSPACE, "this call splits into %lld runs and needs "
+                                "a %zu-byte workspace", (long long)plan.num_ranges, plan.workspace);
     if (workspace_bytes < plan.workspace)
       return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
                   workspace_bytes, plan.workspace);
     if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
-  const int group = q_heads / cache->kv_heads;
   int heads_per_wg = 1;
   for (int w : {PKV_DECODE_HEADS_PER_WG, 4, 2}) {
     if (cache->kv_heads % w == 0) {
@@ -219,23 +261,12 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
       break;
     }
   }
+  const int group = q_heads / cache->kv_heads;
   const int64_t block_bytes =
       (int64_t)cache->block_size * cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype);
   if (block_bytes > UINT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "a block of %lld bytes exceeds 4 GiB", (long long)block_bytes);
-  // A split workgroup walks parts_per_unit consecutive partitions (emitting
-  // each partition's state), as many as keep the grid at the wave target
-  // and the walked table slice within LDS: short partitions then cost no
-  // pipeline restart each.
-  int64_t parts_per_unit = 1;
-  if (plan.num_parts > 1 && PKV_DECODE_WALK_WAVES > 0) {
-    const int64_t lds_cap = (int64_t)pkv::kMaxPartBlocks * cache->block_size / plan.part_tokens;
-    const int64_t fill =
-        (int64_t)num_seqs * cache->kv_heads * plan.num_parts / PKV_DECODE_WALK_WAVES;
-    parts_per_unit = std::max<int64_t>(1, std::min({lds_cap, fill, plan.num_parts}));
-  }
-  const int64_t num_chunks = (plan.num_parts + parts_per_unit - 1) / parts_per_unit;
-  const int64_t units = (int64_t)num_seqs * num_chunks * (cache->kv_heads / heads_per_wg);
+  const int64_t units = plan.num_ranges * (cache->kv_heads / heads_per_wg);
   if (units > INT32_MAX || (int64_t)num_seqs * q_heads > INT32_MAX)
     return fail(PKV_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)units);
 
@@ -246,12 +277,14 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
   a.out = out;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
+  a.plan = nullptr;
   a.part_ml = nullptr;
   a.part_o = nullptr;
   if (plan.workspace > 0) {
-    const int64_t rows = (int64_t)num_seqs * q_heads * plan.num_parts;
-    a.part_ml = static_cast<float*>(workspace);
-    a.part_o = a.part_ml + round_up(2 * rows, 4);
+    char* ws = static_cast<char*>(workspace);
+    a.plan = reinterpret_cast<int32_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + plan.plan_bytes);
+    a.part_o = reinterpret_cast<float*>(ws + plan.plan_bytes + plan.ml_bytes);
   }
   a.num_blocks = cache->num_blocks;
   a.table_width = table_width;
@@ -259,14 +292,12 @@ PKV_EXPORT pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache, 
   a.q_heads = q_heads;
   a.kv_heads = cache->kv_heads;
   a.max_seq_len = max_seq_len;
-  a.part_tokens = (int32_t)plan.part_tokens;
-  a.num_parts = (int32_t)plan.num_parts;
-  a.parts_per_unit = (int32_t)parts_per_unit;
-  a.num_chunks = (int32_t)num_chunks;
+  a.part_tiles = (int32_t)plan.part_tiles;
+  a.num_ranges = (int32_t)plan.num_ranges;
+  a.odd_q10 = (int32_t)plan.odd_q10;
   a.heads_per_wg = heads_per_wg;
   a.row_bytes = (uint32_t)((int64_t)cache->kv_heads * cache->head_dim * elem_bytes(cache->dtype));
   a.tile_bytes = 16u * a.row_bytes;
-  a.block_bytes = (uint32_t)(cache->block_size * (int64_t)a.row_bytes);
   a.scale_log2 = scale * 1.4426950408889634f;
   return from_hip(pkv::launch_decode(a, cache->dtype, cache->head_dim, cache->block_size, group,
                                      (hipStream_t)stream),

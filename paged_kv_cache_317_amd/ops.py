@@ -75,6 +75,16 @@ def decode_partition_tokens(k_cache, num_seqs, q_heads, max_seq_len, part_tokens
     return n
 
 
+def decode_runs(k_cache, num_seqs, q_heads, max_seq_len, part_tokens=0):
+    """Runs (equal shares of the work, one workgroup each per kv-head group)
+    the decode call splits into; 1 means one kernel and no workspace."""
+    desc = cache_desc(k_cache)
+    n = lib().pkv_decode_runs(ctypes.byref(desc), num_seqs, q_heads, max_seq_len, part_tokens)
+    if n == 0:
+        raise ValueError(lib().pkv_last_error().decode())
+    return n
+
+
 def decode_workspace_size(k_cache, num_seqs, q_heads, max_seq_len, part_tokens=0):
     desc = cache_desc(k_cache)
     n = lib().pkv_decode_workspace_size(ctypes.byref(desc), num_seqs, q_heads, max_seq_len,

@@ -86,3 +86,25 @@ def oracle_decode(w, k_cache=None, v_cache=None, seq_lens=None, block_table=None
         w.q, w.k_cache if k_cache is None else k_cache, w.v_cache if v_cache is None else v_cache,
         w.block_table if block_table is None else block_table,
         w.seq_lens if seq_lens is None else seq_lens, cfg.scale, cfg.dtype, seqs=seqs)
+
+
+def drop_bad_blocks(block_table, seq_lens, block_size, num_blocks):
+    """The table and lengths of the sequences with every block whose table
+    entry lies outside the pool taken out (the decode rule for such entries:
+    their positions do not count).  Attention does not depend on the order of
+    positions, so the oracle on the result is the expected output.  Only the
+    last block of a sequence is partial, so a dropped middle block removes
+    block_size positions and a dropped last block the positions it held."""
+    table = np.full_like(block_table, -1)
+    lens = np.array(seq_lens, dtype=np.int32).copy()
+    for s, L in enumerate(np.asarray(seq_lens).tolist()):
+        nb = -(-int(L) // block_size)
+        keep = []
+        for j in range(nb):
+            e = int(block_table[s, j])
+            if 0 <= e < num_blocks:
+                keep.append(e)
+            else:
+                lens[s] -= min(block_size, int(L) - j * block_size)
+        table[s, :len(keep)] = keep
+    return table, lens

@@ -100,28 +100,72 @@ def test_kv_write_and_block_copy_argument_checks():
                                           None)) == "UNSUPPORTED"
 
 
-@pytest.mark.parametrize("S,Hkv,max_len,req,expect", [
-    (256, 8, 4096, 0, 4096),      # enough waves: unsplit
-    (16, 8, 131072, 0, 8192),     # few sequences: split until 2048 waves
-    (16, 8, 131072, 512, 512),    # explicit request
-    (4, 8, 100, 0, 112),          # one partition of the rounded-up length
-    (2, 8, 1_000_000, 0, 4096),   # capped by the LDS table slice, then halved to 2048+ waves
+def _decode_workspace(S, Hkv, G, runs, dtype=1, D=128):
+    """Bytes the split decode needs: the plan (int32: stream prefix [S + 1],
+    shared tiles per group, the run length), padded to 16 bytes; the run
+    states' fp32 (max, sum) pairs, padded to 16 bytes; the fp32 outputs.
+    Slots = runs + groups, each with kv_heads * 16 columns (bf16)."""
+    if runs == 1:
+        return 0
+    gs = 16 // G if dtype == 1 else 1
+    groups = -(-S // gs)
+    rows = (runs + groups) * Hkv * gs * G
+    pad4 = lambda n: -(-n // 4) * 4
+    return pad4(S + 1 + groups + 2) * 4 + pad4(2 * rows) * 4 + rows * D * 4
+
+
+@pytest.mark.parametrize("S,Hkv,max_len,req,part,runs", [
+    (256, 8, 4096, 0, 16, 256),       # the 4k GQA batch: 2048 waves in 256 runs
+    (16, 8, 131072, 0, 16, 272),      # long contexts: runs capped by the 512 tile slots
+    (16, 8, 131072, 512, 512, 272),   # 512-token partitions (32 tiles): 16 per run at most
+    (4, 8, 100, 0, 16, 1),            # 28 tiles at most: one run, no workspace
+    (2, 8, 1_000_000, 0, 16, 256),    # 245 runs would do; 256 kept for the waves
+    (64, 32, 2048, 0, 16, 64),        # 32 kv heads: 64 runs make 2048 waves
+    (3, 1, 4000, 100, 112, 24),       # 7-tile partitions, runs of at least 5: 22, rounded to 24
 ])
-def test_partition_choice(S, Hkv, max_len, req, expect):
+def test_decode_run_choice(S, Hkv, max_len, req, part, runs):
+    """The run count follows the stated rule (about 2048 waves; runs of at
+    least 32 tiles on a full-length batch; from 8 runs on a multiple of 8,
+    odd runs 942/1024 of an even run; the longest run within the 512 tile
+    slots) and the workspace is sized for it."""
     d = _desc(hkv=Hkv)
-    got = lib().pkv_decode_partition_tokens(ctypes.byref(d), S, Hkv * 4, max_len, req)
-    assert got == expect
-    ws = lib().pkv_decode_workspace_size(ctypes.byref(d), S, Hkv * 4, max_len, req)
-    P = -(-max_len // got)
-    rows = S * Hkv * 4 * P
-    # fp32 (max, sum) pairs, padded to 16 bytes, then o per row in the cache
-    # precision (bf16 here: 2 bytes per element)
-    assert ws == (0 if P == 1 else -(-2 * rows // 4) * 4 * 4 + rows * 128 * 2)
+    L = lib()
+    assert L.pkv_decode_partition_tokens(ctypes.byref(d), S, Hkv * 4, max_len, req) == part
+    got = L.pkv_decode_runs(ctypes.byref(d), S, Hkv * 4, max_len, req)
+    assert got == runs
+    pt = part // 16
+    units_bound = S * -(-(-(-max_len // 16)) // pt)
+    if got >= 8:
+        assert got % 8 == 0
+        longest = -(-units_bound * 1024 // ((got // 2) * (1024 + 942)))
+        assert longest * pt <= 512
+    ws = L.pkv_decode_workspace_size(ctypes.byref(d), S, Hkv * 4, max_len, req)
+    assert ws == _decode_workspace(S, Hkv, 4, got)
 
 
-def test_partition_request_rounds_to_block_size():
+def test_decode_workspace_groups_follow_the_head_group():
+    """bf16 columns hold 16 / G sequences' heads; f32 caches one sequence's."""
+    for G in (1, 2, 4, 8):
+        d = _desc(hkv=8)
+        runs = lib().pkv_decode_runs(ctypes.byref(d), 40, 8 * G, 3000, 0)
+        ws = lib().pkv_decode_workspace_size(ctypes.byref(d), 40, 8 * G, 3000, 0)
+        assert runs > 1 and ws == _decode_workspace(40, 8, G, runs)
+    d = _desc(hkv=2, d=64, dtype=0)
+    runs = lib().pkv_decode_runs(ctypes.byref(d), 40, 8, 3000, 0)
+    ws = lib().pkv_decode_workspace_size(ctypes.byref(d), 40, 8, 3000, 0)
+    assert runs > 1 and ws == _decode_workspace(40, 2, 4, runs, dtype=0, D=64)
+
+
+def test_partition_request_rounds_to_16_tokens():
     d = _desc(bs=32)
-    assert lib().pkv_decode_partition_tokens(ctypes.byref(d), 4, 32, 10_000, 100) == 128
+    assert lib().pkv_decode_partition_tokens(ctypes.byref(d), 4, 32, 10_000, 100) == 112
+    assert lib().pkv_decode_partition_tokens(ctypes.byref(d), 4, 32, 10_000, 100_000) == 8192
+
+
+def test_decode_too_many_sequences_for_one_call():
+    d = _desc()
+    assert lib().pkv_decode_runs(ctypes.byref(d), 20_000, 32, 100, 0) == 0
+    assert "sequences" in lib().pkv_last_error().decode()
 
 
 def _extend(desc, S=2, T=40, Hq=32, maxq=20, scale=0.1, q=1 << 12, kc=1 << 12, vc=1 << 12,

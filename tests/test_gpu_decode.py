@@ -119,7 +119,12 @@ def test_placement_permutation_bit_identical(key):
     assert torch.equal(_bits(ref), _bits(got))
 
 
-def test_shared_prefix_equals_private_copies_bit_identical():
+def test_shared_prefix_equals_private_copies():
+    """Sequences that share their prefix blocks give the result of private
+    copies of those blocks.  The shared layout reads each shared block once
+    for the whole group of sequences and the private one reads every copy, so
+    the two agree to the fp32 accumulation (each within the tolerance of the
+    oracle), not bit for bit."""
     w = _case("c4s")
     d = upload(w)
     shared = _decode(d, w)
@@ -141,8 +146,11 @@ def test_shared_prefix_equals_private_copies_bit_identical():
     d["v_cache"] = to_device(vc, "bf16")
     d["block_table"] = to_device(table, None)
     private = _decode(d, w)
-    assert torch.equal(_bits(shared), _bits(private))
-    compare(private, oracle_decode(w, k_cache=kc, v_cache=vc, block_table=table), "bf16")
+    ref = oracle_decode(w)
+    assert np.array_equal(ref, oracle_decode(w, k_cache=kc, v_cache=vc, block_table=table))
+    compare(shared, ref, "bf16")
+    compare(private, ref, "bf16")
+    assert np.abs(out_to_f64(shared) - out_to_f64(private)).max() <= 2e-2
 
 
 @pytest.mark.parametrize("prefix", [1016, 1024])
@@ -174,12 +182,24 @@ def test_copy_on_write_keeps_siblings(prefix):
     # the shared source block is untouched
     assert torch.equal(_bits(d["k_cache"][src]), _bits(src_k))
     assert torch.equal(_bits(d["v_cache"][src]), _bits(src_v))
-    # the sequence that never wrote sees exactly what it saw before; when the
-    # write lands past the old length, so does every writer
+    # The sequence that never wrote sees what it saw before; when the write
+    # lands past the old length, so does every writer.  The copies change
+    # which blocks the group shares, and with it how the work is split, so
+    # "the same" is the oracle's exact equality and the GPU's tolerance.
     after_old = _decode(d, w, seq_lens=lens_b, block_table=ta, max_seq_len=prefix)
-    assert torch.equal(_bits(before[S - 1]), _bits(after_old[S - 1]))
+    ref_before = oracle.decode_attention(w.q, w.k_cache, w.v_cache, sc["table_before"],
+                                         sc["lens_before"], cfg.scale, "bf16")
+    kc0, vc0 = oracle.block_copy(w.k_cache, w.v_cache, sc["pairs"])
+    kc0, vc0 = oracle.kv_write(kc0, vc0, nk[writers], nv[writers], sc["write_slots"][writers],
+                               inplace=True)
+    ref_after_old = oracle.decode_attention(w.q, kc0, vc0, sc["table_after"], sc["lens_before"],
+                                            cfg.scale, "bf16")
+    assert np.array_equal(ref_before[S - 1], ref_after_old[S - 1])
+    compare(before, ref_before, "bf16")
+    compare(after_old[S - 1:], ref_after_old[S - 1:], "bf16")
     if prefix % cfg.block_size:
-        assert torch.equal(_bits(before), _bits(after_old))
+        assert np.array_equal(ref_before, ref_after_old)
+        compare(after_old, ref_after_old, "bf16")
     # writers at the new length match the oracle on the oracle's own copy + write
     kc, vc = oracle.block_copy(w.k_cache, w.v_cache, sc["pairs"])
     kc, vc = oracle.kv_write(kc, vc, nk[writers], nv[writers], sc["write_slots"][writers],
@@ -211,11 +231,12 @@ def test_edge_lengths(lens):
 
 @pytest.mark.parametrize("dtype_case", ["bf16", "f32"])
 @pytest.mark.parametrize("nparts", [2, 3, 4, 5, 8, 9, 16, 17])
-def test_partition_counts_across_both_merges(dtype_case, nparts):
-    """Split calls with 2 .. 17 partitions per sequence: up to 16 take the
-    one-wave-per-row merge, more the four-wave merge.  The batch holds an
-    empty sequence, sequences shorter than one partition, one ending one
-    token into a partition and one filling every partition."""
+def test_partition_lengths_and_merge_counts(dtype_case, nparts):
+    """Short partitions: sequences of 2 .. 17 partitions, so that the merge
+    combines many runs per row (eight states per step, carried across
+    steps).  The batch holds an empty sequence, sequences shorter than one
+    partition, one ending one token into a partition and one filling every
+    partition."""
     if dtype_case == "bf16":
         base = get_config("c3_gqa4k_bf16")
         part = 16
@@ -266,31 +287,3 @@ def test_workspace_errors():
     assert e.value.status_name == "PKV_ERR_WORKSPACE"
 
 
-@pytest.mark.parametrize("dtype_case", ["bf16", "f32"])
-def test_workgroups_walking_several_partitions(dtype_case):
-    """Enough short partitions that each workgroup walks several consecutive
-    ones (emitting every partition's state): the result matches the oracle.
-    A table entry outside the pool at the end of a walked span ends that
-    span there: its last partition carries an empty state, while the
-    sequence's later spans (other workgroups) still count."""
-    if dtype_case == "bf16":
-        cfg = scaled(get_config("c3_gqa4k_bf16"), num_seqs=64, len_range=(200, 512), max_len=512)
-    else:
-        cfg = scaled(get_config("c1_tiny_f32"), num_seqs=64, q_heads=16, kv_heads=8,
-                     seq_lens=(), len_range=(200, 512), max_len=512, pool_blocks=0)
-    w = generate_host(cfg)
-    # 64 sequences x 8 kv heads x 32 partitions of 16 tokens: 8 partitions per workgroup
-    log(f"walk {dtype_case}: S={cfg.num_seqs} part=16")
-    d = upload(w)
-    table = w.block_table.copy()
-    s_bad = 5
-    table[s_bad, 7] = -1                                 # positions >= 112 unreadable
-    out = _decode(d, w, part_tokens=16, block_table=to_device(table, None))
-    # Sequence s_bad attends to positions 0..111 and 128..L-1: the oracle sees
-    # that as a sequence 16 tokens shorter whose table skips logical block 7.
-    ref_table = w.block_table.copy()
-    ref_table[s_bad] = np.concatenate([w.block_table[s_bad, :7], w.block_table[s_bad, 8:], [-1]])
-    lens = w.seq_lens.copy()
-    lens[s_bad] -= cfg.block_size
-    ref = oracle_decode(w, seq_lens=lens, block_table=ref_table)
-    compare(out, ref, cfg.dtype)

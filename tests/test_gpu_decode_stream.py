@@ -1,0 +1,231 @@
+"""Decode work split into equal runs of the work stream, and shared leading
+blocks read once per group of sequences, against the fp64 oracle.
+
+The stream is every sequence's 16-position tiles, sequence after sequence;
+``pkv_decode_runs`` equal runs of it go to the workgroups.  These tests build
+lengths whose run boundaries fall inside sequences, exactly on sequence ends,
+around empty sequences and across table entries outside the pool, and groups
+of sequences (16 / G for bf16 caches) that share leading blocks: whole
+blocks, a partly filled last shared block, a member that ends inside the
+shared blocks, and a last group with fewer members.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_317_amd as pkv
+from workloads.generate import f32_to_bf16_bits
+
+from helpers import compare, drop_bad_blocks, log, out_to_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+# Tiles per sequence 10, 0, 5, 3, 40, 7, 1, 64, 50, 20 (200 in all): with
+# max_seq_len 1024 the call has 24 runs of 9 tiles, so sequence ends land on
+# run boundaries (18, 180), inside runs (10, 15, 58, 65, 66, 130, 200), and
+# sequences sit wholly inside one run (tiles [10, 15), [15, 18), [65, 66)).
+STREAM_LENS = (160, 0, 70, 33, 630, 100, 1, 1024, 790, 305)
+
+
+def _run_starts(total_units, runs):
+    """Run boundaries of the stated rule: from 8 runs on, even runs hold
+    ce = ceil(W * 1024 / ((runs / 2) * (1024 + 942))) partitions and odd
+    runs co = ceil(ce * 942 / 1024); otherwise all hold ceil(W / runs)."""
+    if runs >= 8:
+        ce = max(1, -(-total_units * 1024 // ((runs // 2) * (1024 + 942))))
+        co = max(1, -(-ce * 942 // 1024))
+    else:
+        ce = co = max(1, -(-total_units // runs))
+    return [((r + 1) // 2) * ce + (r // 2) * co for r in range(runs + 1)]
+
+
+def _values(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _batch(rng, lens, BS, Hkv, G, dtype, share=None, width=None):
+    """Pool, table and q for `lens`; ``share`` maps a group's first sequence
+    to (group size, shared block count): those sequences' first blocks are
+    the same physical blocks."""
+    D = 128 if dtype == "bf16" else 64
+    S = len(lens)
+    nblk = [-(-int(L) // BS) for L in lens]
+    MB = width or max(max(nblk), 1)
+    NB = sum(nblk) + 8
+    perm = rng.permutation(NB)
+    table = np.full((S, MB), -1, dtype=np.int32)
+    cur = 0
+    shared_ids = {}
+    for s in range(S):
+        for j in range(nblk[s]):
+            table[s, j] = perm[cur]
+            cur += 1
+    for s0, (gs, nsh) in (share or {}).items():
+        for s in range(s0 + 1, min(s0 + gs, S)):
+            assert nblk[s] >= nsh and nblk[s0] >= nsh
+            table[s, :nsh] = table[s0, :nsh]
+    kc = _values(rng, (NB, BS, Hkv, D), dtype)
+    vc = _values(rng, (NB, BS, Hkv, D), dtype)
+    q = _values(rng, (S, Hkv * G, D), dtype)
+    return kc, vc, table, q
+
+
+def _run(kc, vc, table, q, lens, dtype, scale, max_len, part=0):
+    t = lambda a: to_device(a, dtype if a.dtype in (np.float32, np.uint16) else None)
+    out = pkv.paged_attn_decode(t(q), t(kc), t(vc), t(table), t(np.asarray(lens, np.int32)),
+                                scale, max_len, part_tokens=part)
+    torch.cuda.synchronize()
+    return out
+
+
+def _tile_ends(lens):
+    return np.cumsum([-(-int(L) // 16) for L in lens])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("part", [0, 32, 64])
+def test_runs_cross_sequence_ends(dtype, part):
+    """Runs that end inside a sequence, exactly at a sequence's end, around an
+    empty sequence, and sequences wholly inside one run."""
+    rng = np.random.default_rng(41)
+    BS, Hkv, G = 16, 2, 4
+    kc, vc, table, q = _batch(rng, STREAM_LENS, BS, Hkv, G, dtype)
+    S, max_len = len(STREAM_LENS), 1024
+    runs = pkv.decode_runs(to_device(kc, dtype), S, Hkv * G, max_len, part)
+    if part == 0:
+        # the layout the comment above describes
+        ends = set(_tile_ends(STREAM_LENS).tolist())
+        starts = _run_starts(200, runs)
+        assert runs == 24 and starts[1] == 9
+        inside = [e for e in ends if e not in starts and 0 < e < 200]
+        assert {18, 180} <= ends & set(starts) and inside
+        assert any(starts[r] <= 10 and 15 <= starts[r + 1] for r in range(runs))
+    assert runs > 1
+    log(f"stream {dtype} part={part}: runs={runs}")
+    scale = 0.09
+    got = _run(kc, vc, table, q, STREAM_LENS, dtype, scale, max_len, part)
+    ref = oracle.decode_attention(q, kc, vc, table, np.array(STREAM_LENS), scale, dtype)
+    compare(got, ref, dtype)
+    assert torch.count_nonzero(got[1]) == 0
+
+
+@pytest.mark.parametrize("part", [0, 48, 512])
+def test_runs_skip_table_entries_outside_the_pool(part):
+    """A table entry outside the pool leaves its block's positions out of the
+    sequence, whichever run holds it and however the call splits; other
+    sequences are unaffected."""
+    rng = np.random.default_rng(42)
+    BS, Hkv, G = 16, 2, 4
+    kc, vc, table, q = _batch(rng, STREAM_LENS, BS, Hkv, G, "bf16")
+    NB = kc.shape[0]
+    bad = table.copy()
+    bad[4, 20] = -1          # a middle block of a sequence that crosses runs
+    bad[7, 0] = NB           # the first block of a sequence ending on a boundary
+    bad[8, 49] = NB + 5      # the last (partly filled) block
+    bad[9, 3] = -7
+    t2, l2 = drop_bad_blocks(bad, np.array(STREAM_LENS), BS, NB)
+    scale = 0.09
+    log(f"outside-pool entries part={part}")
+    got = _run(kc, vc, bad, q, STREAM_LENS, "bf16", scale, 1024, part)
+    ref = oracle.decode_attention(q, kc, vc, t2, l2, scale, "bf16")
+    compare(got, ref, "bf16")
+    clean = oracle.decode_attention(q, kc, vc, table, np.array(STREAM_LENS), scale, "bf16")
+    for s in (0, 2, 3, 5, 6):
+        assert np.array_equal(ref[s], clean[s])
+
+
+def _shared_case(rng, G, BS, S, nshared):
+    """S sequences in groups of 16 / G; group k shares nshared[k] leading
+    blocks.  Member lengths put one member's end inside the last shared block
+    where that is possible, one exactly at the end of the shared blocks, and
+    the rest past them."""
+    gs = 16 // G
+    lens = []
+    for s in range(S):
+        k, m = divmod(s, gs)
+        J = nshared[k % len(nshared)]
+        if J == 0:
+            lens.append(int(rng.integers(1, 300)))
+        elif m == 1:
+            lens.append((J - 1) * BS + int(rng.integers(1, BS + 1)))   # ends in block J-1
+        elif m == 2:
+            lens.append(J * BS)
+        else:
+            lens.append(J * BS + int(rng.integers(1, 300)))
+    share = {}
+    for k in range(-(-S // gs)):
+        J = nshared[k % len(nshared)]
+        if J and min(gs, S - k * gs) >= 2:
+            share[k * gs] = (gs, J)
+    return lens, share
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("BS", [16, 32])
+def test_shared_prefix_groups(G, BS):
+    """Groups of 16 / G sequences sharing 0, 1, 3 or 20 leading blocks (the
+    shared blocks are read once per group), a partial last group, members
+    ending inside or at the end of the shared blocks; both the library's
+    split and 64-token partitions."""
+    rng = np.random.default_rng(1000 + G * 10 + BS)
+    gs = 16 // G
+    S = 3 * gs + max(1, gs // 2) + (1 if gs == 1 else 0)
+    lens, share = _shared_case(rng, G, BS, S, nshared=[20, 3, 0, 1])
+    Hkv = 2
+    kc, vc, table, q = _batch(rng, lens, BS, Hkv, G, "bf16", share=share)
+    max_len = int(max(lens))
+    scale = 0.08
+    ref = oracle.decode_attention(q, kc, vc, table, np.array(lens), scale, "bf16")
+    for part in (0, 64):
+        log(f"shared G={G} BS={BS} S={S} part={part} lens={lens[:6]}")
+        got = _run(kc, vc, table, q, lens, "bf16", scale, max_len, part)
+        compare(got, ref, "bf16")
+
+
+def test_shared_prefix_with_out_of_pool_entry_and_long_groups():
+    """A group whose shared run stops at an entry outside the pool (it is
+    not shared; its positions are left out for the member that holds it),
+    and groups whose shared prefix is longer than one 64-block comparison
+    round (130 blocks)."""
+    rng = np.random.default_rng(77)
+    G, BS = 4, 16
+    lens = [130 * 16 + 40, 130 * 16 + 7, 130 * 16, 129 * 16 + 3,
+            300, 290, 310, 280]
+    share = {0: (4, 130), 4: (4, 12)}
+    kc, vc, table, q = _batch(rng, lens, BS, 2, G, "bf16", share=share)
+    NB = kc.shape[0]
+    table[5, 6] = -1            # member 1 of group 1 holds a bad entry in the shared run
+    t2, l2 = drop_bad_blocks(table, np.array(lens), BS, NB)
+    scale = 0.08
+    ref = oracle.decode_attention(q, kc, vc, t2, l2, scale, "bf16")
+    for part in (0, 16, 512):
+        got = _run(kc, vc, table, q, lens, "bf16", scale, int(max(lens)), part)
+        compare(got, ref, "bf16")
+
+
+def test_shared_and_private_layouts_agree():
+    """The same data as one group sharing 40 blocks and as private copies:
+    both match the oracle (which gives the same values for both) and each
+    other within the tolerance."""
+    rng = np.random.default_rng(5)
+    G, BS = 4, 16
+    lens = [40 * 16 + 100, 40 * 16 + 3, 40 * 16 + 250, 40 * 16 + 1]
+    kc, vc, table, q = _batch(rng, lens, BS, 8, G, "bf16", share={0: (4, 40)})
+    NB = kc.shape[0]
+    kp = np.concatenate([kc, kc[table[0, :40]], kc[table[0, :40]], kc[table[0, :40]]])
+    vp = np.concatenate([vc, vc[table[0, :40]], vc[table[0, :40]], vc[table[0, :40]]])
+    tp = table.copy()
+    for i, s in enumerate((1, 2, 3)):
+        tp[s, :40] = NB + 40 * i + np.arange(40)
+    scale = 0.08
+    ref = oracle.decode_attention(q, kc, vc, table, np.array(lens), scale, "bf16")
+    assert np.array_equal(ref, oracle.decode_attention(q, kp, vp, tp, np.array(lens), scale,
+                                                       "bf16"))
+    a = _run(kc, vc, table, q, lens, "bf16", scale, int(max(lens)))
+    b = _run(kp, vp, tp, q, lens, "bf16", scale, int(max(lens)))
+    compare(a, ref, "bf16")
+    compare(b, ref, "bf16")
+    assert np.abs(out_to_f64(a) - out_to_f64(b)).max() <= 2e-2

@@ -1,9 +1,8 @@
 """The five workloads at full size, in the launch configuration bench.py times.
 
-Small pools (c1, c2, c4) are generated on the host and every output is
-compared with the oracle.  Large pools (c3, c5) are drawn on the device; the
-pools are copied back and the oracle computes a seeded sample of sequences
-(plus the shortest and the longest) one by one.
+Small pools (c1, c2, c4) are generated on the host; large pools (c3, c5) are
+drawn on the device and copied back.  Every output row of every workload is
+compared with the oracle.
 """
 
 import numpy as np
@@ -44,8 +43,8 @@ def test_full_config_host_generated(name):
     log(f"  max-abs {mabs:.3e} row max-rel {mrel:.3e}")
 
 
-@pytest.mark.parametrize("name,nsample", [("c3_gqa4k_bf16", 8), ("c5_long_bf16", 1)])
-def test_full_config_device_generated_sampled(name, nsample):
+@pytest.mark.parametrize("name", ["c3_gqa4k_bf16", "c5_long_bf16"])
+def test_full_config_device_generated(name):
     cfg = get_config(name)
     w = generate_device(cfg)
     lay = w.layout
@@ -56,6 +55,7 @@ def test_full_config_device_generated_sampled(name, nsample):
     torch.cuda.synchronize()
     k0 = to_host(w.k_cache, cfg.dtype)
     v0 = to_host(w.v_cache, cfg.dtype)
+    q = to_host(w.q, cfg.dtype)
     out = _step(d, cfg, lay.max_seq_len)
     # the slot write, bit for bit, on the rows it touched and on the whole pool
     slots = to_host(w.slot_mapping, None)
@@ -63,13 +63,6 @@ def test_full_config_device_generated_sampled(name, nsample):
     oracle.kv_write(k0, v0, new_k, new_v, slots, inplace=True)
     assert np.array_equal(to_host(d["k_cache"], cfg.dtype), k0)
     assert np.array_equal(to_host(d["v_cache"], cfg.dtype), v0)
-    rng = np.random.default_rng(cfg.seed)
-    lens = lay.seq_lens
-    pick = set(rng.choice(cfg.num_seqs, size=nsample, replace=False).tolist())
-    pick |= {int(np.argmin(lens)), int(np.argmax(lens))}
-    seqs = sorted(pick)
-    q = to_host(w.q, cfg.dtype)
-    ref = oracle.decode_attention(q, k0, v0, lay.block_table, lens, cfg.scale, cfg.dtype,
-                                  seqs=seqs)
-    mabs, mrel = compare(out, ref, cfg.dtype, rows=seqs)
-    log(f"  sampled {seqs}: max-abs {mabs:.3e} row max-rel {mrel:.3e}")
+    ref = oracle.decode_attention(q, k0, v0, lay.block_table, lay.seq_lens, cfg.scale, cfg.dtype)
+    mabs, mrel = compare(out, ref, cfg.dtype)
+    log(f"  all {cfg.num_seqs} sequences: max-abs {mabs:.3e} row max-rel {mrel:.3e}")
