@@ -175,6 +175,33 @@ pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and result as
+ * pkv_paged_attn_decode, with the split workspace taken from a device array
+ * of the library (pkv_decode_noalloc_max_workspace() bytes, 64 MiB) instead
+ * of caller memory.  Each GPU holds its own array from the first call on it
+ * until the process ends.  Calls needing more than that (see
+ * pkv_decode_workspace_size) return PKV_ERR_WORKSPACE before any HIP call.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (several streams or threads at once) race and may corrupt each other's
+ * results.  Nothing in the array needs clearing between calls.
+ */
+pkv_status pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache,
+                                         const void* v_cache,
+                                         const pkv_cache_desc* cache,
+                                         const int32_t* block_table,
+                                         int32_t table_width,
+                                         const int32_t* seq_lens,
+                                         int32_t num_seqs, int32_t q_heads,
+                                         int32_t max_seq_len, float scale,
+                                         void* out, int32_t part_tokens,
+                                         void* stream);
+
+/* Bytes of the array pkv_paged_attn_decode_noalloc uses per GPU. */
+size_t pkv_decode_noalloc_max_workspace(void);
+
+/*
  * Attention of several new tokens per sequence over a paged cache: a prefill
  * (nothing cached yet), or a chunk of new tokens on top of a cached context.
  * The new tokens' K/V rows must already be in the cache (pkv_paged_kv_write).

@@ -15,6 +15,7 @@ from .ops import (
     extend_partition_tokens,
     extend_workspace_size,
     paged_attn_decode,
+    paged_attn_decode_noalloc,
     paged_attn_extend,
     paged_block_copy,
     paged_block_move,
@@ -32,6 +33,7 @@ __all__ = [
     "extend_partition_tokens",
     "extend_workspace_size",
     "paged_attn_decode",
+    "paged_attn_decode_noalloc",
     "paged_attn_extend",
     "paged_block_copy",
     "paged_block_move",

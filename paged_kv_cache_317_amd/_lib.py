@@ -52,6 +52,9 @@ SIGNATURES = {
     "pkv_paged_kv_write": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _desc, _vp]),
     "pkv_paged_attn_decode": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32, _i32,
                                      _f32, _vp, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attn_decode_noalloc": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _i32, _i32,
+                                             _i32, _f32, _vp, _i32, _vp]),
+    "pkv_decode_noalloc_max_workspace": (_sz, []),
     "pkv_paged_attn_extend": (_i32, [_vp, _vp, _vp, _desc, _vp, _i32, _vp, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _f32, _vp, _i32, _vp, _sz, _vp]),
     "pkv_extend_partition_tokens": (_i32, [_desc, _i32, _i32, _i32, _i32, _i32, _i32]),

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_decode.hip", "attn_extend.hip", "kv_write.hip", "block_copy.hip", "pkv_api.cpp", "block_manager.cpp"]
+SOURCES = ["attn_decode.hip", "attn_extend.hip", "kv_write.hip", "block_copy.hip",
+           "decode_noalloc.hip", "pkv_api.cpp", "block_manager.cpp"]
 
 # Packed fp32 instructions are kept out of the generated code on purpose.
 HIP_FLAGS = [

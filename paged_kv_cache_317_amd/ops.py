@@ -131,6 +131,31 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale, max_seq
     return out
 
 
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, scale, max_seq_len,
+                              out, part_tokens=0):
+    """``paged_attn_decode`` for callers that cannot allocate: ``out`` must be
+    given, and the split workspace is the library's own device array (calls
+    needing more than ``pkv_decode_noalloc_max_workspace()`` bytes raise).
+    Calls overlapping on one GPU race."""
+    desc = _check_caches(k_cache, v_cache)
+    dev = k_cache.device
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs, q_heads, head_dim]")
+    S, Hq, D = q.shape
+    _require(q, "q", dev, k_cache.dtype, (S, Hq, desc.head_dim))
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, table_width]")
+    _require(block_table, "block_table", dev, torch.int32, (S, block_table.shape[1]))
+    _require(seq_lens, "seq_lens", dev, torch.int32, (S,))
+    _require(out, "out", dev, q.dtype, q.shape)
+    with torch.cuda.device(dev):
+        check(lib().pkv_paged_attn_decode_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), S, Hq, int(max_seq_len), float(scale),
+            _ptr(out), int(part_tokens), _stream(dev)))
+    return out
+
+
 def extend_partition_tokens(k_cache, num_seqs, num_tokens, q_heads, max_query_len,
                             max_seq_len, part_tokens=0):
     desc = cache_desc(k_cache)
