@@ -355,6 +355,11 @@ typedef struct {
   int64_t host_blocks_used; /* swap space holding swapped-out blocks         */
   int64_t swapped_sequences;
   int64_t swap_outs;        /* pkv_bm_swap_out calls so far                  */
+  int64_t unused_slots;     /* allocated_slots - used_slots: slots reserved
+                               but holding no token ("What does PagedAttention
+                               change in LLM KV allocation?", "Calculate
+                               unused block space")                        */
+  double waste_fraction;    /* unused_slots / allocated_slots (0 if none)    */
 } pkv_bm_stats;
 
 /* Create a manager for num_blocks blocks of block_size slots.  free_order

@@ -31,7 +31,8 @@ Modules
                    attend), the split-K partition states and their merge.
 ``extend``         multi-token (prefill / chunked extend) causal attention
                    over a paged cache.
-``cache_ops``      slot write and block copy (bitwise).
+``cache_ops``      slot write, block copy and the two-pool block move
+                   (bitwise).
 ``block_manager``  on-demand allocation, reference counts, copy-on-write,
                    release, and waste accounting.
 
@@ -50,7 +51,7 @@ from .attention import (
     split_decode_attention,
 )
 from .extend import extend_attention, extend_flops
-from .cache_ops import kv_write, block_copy
+from .cache_ops import kv_write, block_copy, block_move
 from .block_manager import BlockManager, OutOfBlocks, blocks_for, tail_waste
 
 __all__ = [
@@ -64,6 +65,7 @@ __all__ = [
     "extend_flops",
     "kv_write",
     "block_copy",
+    "block_move",
     "BlockManager",
     "OutOfBlocks",
     "blocks_for",

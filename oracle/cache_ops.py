@@ -16,8 +16,16 @@
   are distinct and none equals any ``src``, so the order of pairs does not
   matter.
 
-Both operate on raw stored values (float32 or uint16 bit patterns) and never
-round or convert anything.
+* Block move: the same copy between two pools of one block shape, the mover
+  behind swapping a preempted sequence's blocks out to host memory and back
+  ("PagedAttention Explained", "Preemption and scheduling" names swapping as
+  one answer to running out of blocks).  For every ``(src, dst)`` pair, block
+  ``dst`` of the destination pool becomes block ``src`` of the source pool as
+  it was before the call.  Reading: ids outside their pool are an error here
+  (the device library skips them as a guard).
+
+All three operate on raw stored values (float32 or uint16 bit patterns) and
+never round or convert anything.
 """
 
 import numpy as np
@@ -61,3 +69,26 @@ def block_copy(k_cache, v_cache, pairs, inplace=False):
     k_cache[dst] = k_src
     v_cache[dst] = v_src
     return k_cache, v_cache
+
+
+def block_move(src_k, src_v, dst_k, dst_v, pairs):
+    """Copy blocks ``src`` of (src_k, src_v) to blocks ``dst`` of (dst_k,
+    dst_v); returns new destination pools.  ``pairs`` is ``[n, 2]`` of
+    ``(src, dst)``; destination ids must be distinct.  When the two pools are
+    the same arrays, the sources are read before any write."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    src, dst = pairs[:, 0], pairs[:, 1]
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools must have the same block shape and dtype")
+    if len(set(dst.tolist())) != len(dst):
+        raise ValueError("destination ids must be distinct")
+    if src.size and (src.min() < 0 or src.max() >= src_k.shape[0]
+                     or dst.min() < 0 or dst.max() >= dst_k.shape[0]):
+        raise IndexError("a block id is outside its pool")
+    k_rows = src_k[src].copy()
+    v_rows = src_v[src].copy()
+    out_k = dst_k.copy()
+    out_v = dst_v.copy()
+    out_k[dst] = k_rows
+    out_v[dst] = v_rows
+    return out_k, out_v

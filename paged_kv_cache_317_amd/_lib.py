@@ -31,7 +31,8 @@ class BmStats(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "allocated_blocks", "allocated_slots", "used_slots", "free_blocks", "sequences",
         "logical_tokens", "copies", "preemptions", "cached_blocks", "reused_blocks",
-        "host_blocks_used", "swapped_sequences", "swap_outs")]
+        "host_blocks_used", "swapped_sequences", "swap_outs", "unused_slots")] + [
+        ("waste_fraction", ctypes.c_double)]
 
 
 class PkvError(RuntimeError):

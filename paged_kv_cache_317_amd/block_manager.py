@@ -123,11 +123,7 @@ class BlockManager:
     def stats(self):
         s = BmStats()
         check(lib().pkv_bm_get_stats(self._h, ctypes.byref(s)))
-        d = {name: int(getattr(s, name)) for name, _ in BmStats._fields_}
-        d["unused_slots"] = d["allocated_slots"] - d["used_slots"]
-        d["waste_fraction"] = (d["unused_slots"] / d["allocated_slots"]
-                               if d["allocated_slots"] else 0.0)
-        return d
+        return {name: getattr(s, name) for name, _ in BmStats._fields_}
 
 
 def capacity(num_blocks, block_size, lens, reserve_len):

@@ -72,11 +72,17 @@ __global__ __launch_bounds__(kThreads) void block_move_kernel(BlockMoveArgs a, i
 
 }  // namespace
 
+int64_t block_move_workgroups(const BlockMoveArgs& a) {
+  const int64_t block_vecs = a.block_bytes >> 4;
+  return (int64_t)a.num_pairs * 2 * ((block_vecs + kChunkVecs - 1) / kChunkVecs);
+}
+
 hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream) {
   if (a.num_pairs == 0) return hipSuccess;
   const int64_t block_vecs = a.block_bytes >> 4;
   const int chunks = (int)((block_vecs + kChunkVecs - 1) / kChunkVecs);
-  const int64_t grid = (int64_t)a.num_pairs * 2 * chunks;
+  const int64_t grid = block_move_workgroups(a);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (a.streaming)
     hipLaunchKernelGGL(block_move_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        a, chunks);

@@ -461,6 +461,9 @@ PKV_EXPORT pkv_status pkv_bm_get_stats(const pkv_block_manager* bm, pkv_bm_stats
   s.host_blocks_used = bm->host_blocks - (int64_t)bm->host_free.size();
   s.swapped_sequences = (int64_t)bm->swapped.size();
   s.swap_outs = bm->swap_outs;
+  s.unused_slots = s.allocated_slots - s.used_slots;
+  s.waste_fraction =
+      s.allocated_slots > 0 ? (double)s.unused_slots / (double)s.allocated_slots : 0.0;
   *out = s;
   return ok();
 }

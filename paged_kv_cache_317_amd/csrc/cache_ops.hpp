@@ -34,6 +34,9 @@ struct BlockMoveArgs {
 };
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+// Workgroups launch_block_move starts for these arguments (the API refuses
+// calls above INT32_MAX before launching).
+int64_t block_move_workgroups(const BlockMoveArgs& a);
 hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream);
 
 }  // namespace pkv

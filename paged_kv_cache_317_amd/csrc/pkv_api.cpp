@@ -492,8 +492,7 @@ PKV_EXPORT pkv_status pkv_paged_block_copy(const int64_t* pairs, int32_t num_pai
   a.streaming = true;
   a.block_bytes = (int64_t)cache->block_size * cache->kv_heads * cache->head_dim *
                   elem_bytes(cache->dtype);
-  const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
-  if ((int64_t)num_pairs * 2 * chunks > INT32_MAX)
+  if (pkv::block_move_workgroups(a) > INT32_MAX)
     return fail(PKV_ERR_SHAPE, "too many pairs for one launch");
   return from_hip(pkv::launch_block_move(a, (hipStream_t)stream), "paged_block_copy launch");
 }
@@ -562,8 +561,7 @@ PKV_EXPORT pkv_status pkv_paged_block_move(const int64_t* pairs, int32_t num_pai
   a.src_blocks = src->num_blocks;
   a.dst_blocks = dst->num_blocks;
   a.block_bytes = (int64_t)src->block_size * src->kv_heads * src->head_dim * elem_bytes(src->dtype);
-  const int64_t chunks = (a.block_bytes / 16 + 1023) / 1024;
-  if ((int64_t)num_pairs * 2 * chunks > INT32_MAX)
+  if (pkv::block_move_workgroups(a) > INT32_MAX)
     return fail(PKV_ERR_SHAPE, "too many pairs for one launch");
   a.streaming = false;
   return from_hip(pkv::launch_block_move(a, (hipStream_t)stream), "paged_block_move launch");

@@ -252,3 +252,13 @@ def test_block_move_argument_checks_run_before_any_launch():
                       ctypes.byref(b), None)) == "ALIGN"
     assert _status(mv(None, 0, None, None, ctypes.byref(a), None, None, ctypes.byref(b),
                       None)) == "OK"
+
+
+def test_block_copy_launch_size_guard_uses_the_kernel_chunk():
+    """A 64 KiB block is two 32 KiB copy chunks per pool, four workgroups per
+    pair: 600 million pairs exceed the grid and are refused before any
+    launch; the guard counts the kernel's own chunk size."""
+    L = lib()
+    d64 = _desc(bs=32, hkv=8, d=128, dtype=1)
+    st = L.pkv_paged_block_copy(1 << 12, 600_000_000, 1 << 12, 1 << 12, ctypes.byref(d64), None)
+    assert _status(st) == "SHAPE" and "too many pairs" in L.pkv_last_error().decode()

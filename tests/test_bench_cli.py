@@ -58,6 +58,8 @@ def test_oracle_timing_runs_in_a_child_with_a_worker_pool():
     res = bench.cpu_baseline(cfg, w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, 4)
     assert res["kind"] == "oracle" and res["unit"] == "GB/s"
     assert 1 <= res["cores"] <= min(4, bench.host_workers())
+    assert res["workers"] == res["cores"] and res["visible_cores"] == bench.visible_cores()
+    assert bench.host_workers() == min(bench.visible_cores(), res["core_share"])
     assert res["value"] > 0 and res["one_core"]["value"] > 0
     with pytest.raises(RuntimeError):
         bench.run_cpu_oracle("decode", {"q": w.q}, [0], scale=0.1, dtype="f32")

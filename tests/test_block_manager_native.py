@@ -28,6 +28,7 @@ def _same_state(nat, orc, live, width):
               "free_blocks", "sequences"):
         assert a[k] == b[k], k
     assert a["logical_tokens"] == sum(orc.lengths.values())
+    assert abs(a["waste_fraction"] - b["waste_fraction"]) <= 1e-12
 
 
 def test_worked_example_35_tokens():

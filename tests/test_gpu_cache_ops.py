@@ -204,9 +204,8 @@ def test_block_move_device_host_device_bit_exact(name, kw):
     hv = _pinned_pool((HB,) + tuple(d["v_cache"].shape[1:]), d["v_cache"].dtype)
     pkv.paged_block_move(to_device(out_pairs, None), d["k_cache"], d["v_cache"], hk, hv)
     torch.cuda.synchronize()
-    ek = np.zeros((HB,) + w.k_cache.shape[1:], w.k_cache.dtype)
-    ev = np.zeros_like(ek)
-    ek[host], ev[host] = w.k_cache[src], w.v_cache[src]
+    zeros = np.zeros((HB,) + w.k_cache.shape[1:], w.k_cache.dtype)
+    ek, ev = oracle.block_move(w.k_cache, w.v_cache, zeros, zeros, out_pairs)
     assert np.array_equal(to_host(hk, cfg.dtype), ek)
     assert np.array_equal(to_host(hv, cfg.dtype), ev)
     # back into other device blocks; pairs in pinned host memory this time
@@ -215,8 +214,7 @@ def test_block_move_device_host_device_bit_exact(name, kw):
     log(f"block_move h2d {name} pairs={len(in_pairs)}")
     pkv.paged_block_move(in_pairs, hk, hv, d["k_cache"], d["v_cache"])
     torch.cuda.synchronize()
-    rk, rv = w.k_cache.copy(), w.v_cache.copy()
-    rk[dst], rv[dst] = w.k_cache[src], w.v_cache[src]
+    rk, rv = oracle.block_move(ek, ev, w.k_cache, w.v_cache, in_pairs.numpy())
     assert np.array_equal(to_host(d["k_cache"], cfg.dtype), rk)
     assert np.array_equal(to_host(d["v_cache"], cfg.dtype), rv)
 

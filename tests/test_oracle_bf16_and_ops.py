@@ -114,3 +114,53 @@ def test_block_copy_rejects_overlapping_pairs():
         oracle.block_copy(kc, kc, [[0, 1], [2, 1]])      # duplicate dst
     with pytest.raises(ValueError):
         oracle.block_copy(kc, kc, [[0, 1], [1, 2]])      # dst is also a src
+
+
+def test_block_move_matches_an_element_loop_and_round_trips():
+    """Two pools of one block shape: every element of each destination block
+    is the source block's, element by element (a plain loop, no numpy
+    indexing); blocks not named as a destination keep their bits; moving out
+    then back into the same ids restores the first pool."""
+    rng = np.random.default_rng(9)
+    dev_k = rng.integers(0, 1 << 16, size=(12, 4, 2, 3), dtype=np.uint16)
+    dev_v = rng.integers(0, 1 << 16, size=(12, 4, 2, 3), dtype=np.uint16)
+    host_k = np.zeros((5, 4, 2, 3), np.uint16)
+    host_v = np.zeros((5, 4, 2, 3), np.uint16)
+    pairs = [(7, 0), (2, 3), (11, 1)]
+    hk, hv = oracle.block_move(dev_k, dev_v, host_k, host_v, pairs)
+    for b in range(5):
+        src = dict((d, s) for s, d in pairs).get(b)
+        for i in range(4):
+            for j in range(2):
+                for e in range(3):
+                    want_k = dev_k[src, i, j, e] if src is not None else 0
+                    want_v = dev_v[src, i, j, e] if src is not None else 0
+                    assert hk[b, i, j, e] == want_k and hv[b, i, j, e] == want_v
+    # back into other device blocks, then into the original ones
+    cleared_k, cleared_v = dev_k.copy(), dev_v.copy()
+    for s, _ in pairs:
+        cleared_k[s] = 0
+        cleared_v[s] = 0
+    back_k, back_v = oracle.block_move(hk, hv, cleared_k, cleared_v, [(d, s) for s, d in pairs])
+    assert np.array_equal(back_k, dev_k) and np.array_equal(back_v, dev_v)
+
+
+def test_block_move_within_one_pool_is_block_copy():
+    rng = np.random.default_rng(10)
+    k = rng.standard_normal((9, 4, 2, 3)).astype(np.float32)
+    v = rng.standard_normal((9, 4, 2, 3)).astype(np.float32)
+    pairs = [(1, 4), (1, 5), (8, 0)]
+    mk, mv = oracle.block_move(k, v, k, v, pairs)
+    ck, cv = oracle.block_copy(k, v, pairs)
+    assert np.array_equal(mk, ck) and np.array_equal(mv, cv)
+
+
+def test_block_move_rejects_bad_pairs():
+    k = np.zeros((4, 2, 1, 2), np.float32)
+    h = np.zeros((2, 2, 1, 2), np.float32)
+    with pytest.raises(IndexError):
+        oracle.block_move(k, k, h, h, [(3, 2)])
+    with pytest.raises(ValueError):
+        oracle.block_move(k, k, h, h, [(0, 1), (2, 1)])
+    with pytest.raises(ValueError):
+        oracle.block_move(k, k, np.zeros((2, 4, 1, 2), np.float32), h, [(0, 1)])

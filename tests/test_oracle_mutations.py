@@ -66,6 +66,13 @@ MUTATIONS = {
     "slot decode swapped": (
         "cache_ops.py", "        block, offset = divmod(slot, block_size)",
         "        offset, block = divmod(slot, block_size)", "test_oracle_bf16_and_ops.py"),
+    "block move writes K rows into V": (
+        "cache_ops.py", "    out_v[dst] = v_rows\n", "    out_v[dst] = k_rows\n",
+        "test_oracle_bf16_and_ops.py"),
+    "block move reads the block after the source": (
+        "cache_ops.py", "    k_rows = src_k[src].copy()\n",
+        "    k_rows = src_k[np.minimum(src + 1, src_k.shape[0] - 1)].copy()\n",
+        "test_oracle_bf16_and_ops.py"),
     "block copy skips V": (
         "cache_ops.py", "    k_cache[dst] = k_src\n    v_cache[dst] = v_src",
         "    k_cache[dst] = k_src", "test_oracle_bf16_and_ops.py"),

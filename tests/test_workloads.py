@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from workloads import CONFIGS, build_layout, cow_layout, generate_host, get_config, \
-    f32_to_bf16_bits, decode_slots
+    f32_to_bf16_bits, decode_slots, scaled
 
 
 def test_bf16_rounding_is_nearest_even():
@@ -142,3 +142,46 @@ def test_extend_slots_of_a_hand_made_table():
     slots = extend_slots(table, np.array([6, 9]), np.array([0, 3, 5]), 4)
     # sequence 0: positions 3, 4, 5; sequence 1: positions 7, 8
     assert slots.tolist() == [5 * 4 + 3, 2 * 4 + 0, 2 * 4 + 1, 7 * 4 + 3, 3 * 4 + 0]
+
+
+def test_decode_slot_of_the_35_token_example():
+    """The worked example of "What does PagedAttention change in LLM KV
+    allocation?" ("Calculate unused block space"): 35 tokens at block size
+    16 fill blocks 16, 16 and 3, so the newest token (position 34) is the
+    third slot of logical block 2, whatever physical block that is."""
+    import json
+    import os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "worked_example_35_tokens.json")))
+    bs, n = fx["block_size"], fx["tokens"]
+    last_block = len(fx["block_fill"]) - 1
+    offset = fx["block_fill"][-1] - 1
+    table = np.array([[40, 7, 23, -1]], dtype=np.int32)
+    slot = decode_slots(table, np.array([n]), bs)[0]
+    assert slot == table[0, last_block] * bs + offset == 23 * 16 + 2
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("c1_tiny_f32", {}),
+    ("c2_mha_bf16", dict(num_seqs=9, len_range=(1, 700), max_len=704)),
+    ("c5_long_bf16", dict(num_seqs=3, len_range=(1, 3000), max_len=3072)),
+])
+def test_decode_slots_match_the_oracle_block_manager(name, kw):
+    """The generator's slot for each sequence's newest token is the slot the
+    oracle's block manager hands out for that token when it appends every
+    token of the same sequences (blocks taken in the layout's placement
+    order), and the manager's tables are the layout's."""
+    import oracle
+    cfg = scaled(get_config(name), **kw)
+    lay = build_layout(cfg)
+    BS, S = cfg.block_size, cfg.num_seqs
+    order = [int(b) for b in lay.block_table.ravel() if b >= 0] + [int(b) for b in lay.spare_blocks]
+    bm = oracle.BlockManager(lay.num_blocks, BS, free_order=order)
+    last = []
+    for s in range(S):
+        bm.add(s)
+        slots, copies = bm.append(s, int(lay.seq_lens[s]))
+        assert copies == []
+        last.append(slots[-1])
+    assert np.array_equal(bm.table_array(range(S), cfg.table_width), lay.block_table)
+    assert np.array_equal(decode_slots(lay.block_table, lay.seq_lens, BS), np.array(last))
