@@ -83,6 +83,11 @@ constexpr uint32_t kNoTile = 0xfffffffeu;    // partition slot past a member's t
 // Running max of a column that has seen no token yet: finite, so that a tile
 // on which a column is masked leaves its state exactly as it was.
 constexpr float kStateFloor = -1.0e30f;
+// Fourth word of a buffer resource for raw accesses: 32-bit data format, no
+// swizzle, no stride (num_records then counts bytes).
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: the non-temporal bit.
+constexpr int kLoadNonTemporal = 2;
 // Kv heads (one wave each) a decode workgroup can hold.
 #ifndef PKV_DECODE_MAX_WAVES
 #define PKV_DECODE_MAX_WAVES 4
@@ -525,40 +530,40 @@ void decode_stream_kernel(DecodeArgs a) {
     reset_state();
   };
 
-  auto load_tile = [&](uint32_t taddr, u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
+  // Loads of one tile.  Tiles every member of a group reads go through the
+  // caches (`cached`); every other tile is read once per call and kv head
+  // and is loaded non-temporally.  Buffer loads over the tile's 16 rows: the
+  // cache policy is an immediate of the instruction, so the two flavours are
+  // two instruction sequences under one uniform branch.
+  auto load_tile = [&](uint32_t taddr, bool cached, u32x4_t (&kr)[4], u32x4_t (&vr)[4]) {
     // A table entry outside the pool reads tile 0 instead (in the pool); its
     // tokens are masked.
     const uint32_t t = (uint32_t)uniform_int((int)(taddr >= kNoTile ? 0u : taddr));
     const uint64_t base = (uint64_t)t * a.tile_bytes;
-    const char* kp = kcache + base;
-    const char* vp = vcache + base;
-    // The offsets are re-materialised here so that each load is selected as
-    // SGPR base + 32-bit VGPR offset rather than a 64-bit VGPR address.
-    auto ld = [](const char* p) {
-      return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    };
-    if constexpr (kBf16) {
-      uint32_t v0 = v_lane0, v1 = v_lane0 + row_u32, v2 = v_lane0 + 2 * row_u32,
-               v3 = v_lane0 + 3 * row_u32;
-      asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
-      kr[0] = ld(kp + v0);
-      kr[1] = ld(kp + v1);
-      kr[2] = ld(kp + v2);
-      kr[3] = ld(kp + v3);
-      vr[0] = ld(vp + v0);
-      vr[1] = ld(vp + v1);
-      vr[2] = ld(vp + v2);
-      vr[3] = ld(vp + v3);
-    } else {
-      uint32_t kl = k_lane, v0 = v_lane0, v1 = v_lane0 + row_u32, v2 = v_lane0 + 2 * row_u32,
-               v3 = v_lane0 + 3 * row_u32;
-      asm volatile("" : "+v"(kl), "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kcache + base), 0, a.tile_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(vcache + base), 0, a.tile_bytes, kBufferWord3);
+    uint32_t koff[4], voff[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kr[c] = ld(kp + kl + c * 64);
-      vr[0] = ld(vp + v0);
-      vr[1] = ld(vp + v1);
-      vr[2] = ld(vp + v2);
-      vr[3] = ld(vp + v3);
+    for (int i = 0; i < 4; ++i) {
+      koff[i] = kBf16 ? v_lane0 + i * row_u32 : k_lane + 64 * i;
+      voff[i] = v_lane0 + i * row_u32;
+    }
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0));
+        vr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kr[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, kLoadNonTemporal));
+        vr[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, kLoadNonTemporal));
+      }
     }
   };
 
@@ -738,8 +743,10 @@ void decode_stream_kernel(DecodeArgs a) {
   // ---- walk the run's tiles ----
   // Pieces: the run's tiles of one member, and for member 0 of a sharing
   // group its shared and its private tiles as two pieces.  Per piece the
-  // member, its length and the column masks are fixed, so the tile loop
-  // reads only the next tile's staged address from LDS.
+  // member, its length, the column masks and the load flavour are fixed, so
+  // the tile loop reads only the next tile's staged address from LDS.  The
+  // load issued for the first tile of the next piece takes the current
+  // piece's flavour.
   int i = 0;
   while (i < nslots && s_addr[i] == kNoTile) ++i;
   if (i < nslots) {
@@ -747,7 +754,7 @@ void decode_stream_kernel(DecodeArgs a) {
     int k_cur = -1;
     u32x4_t kr[4], vr[4];
     uint32_t taddr = (uint32_t)uniform_int((int)s_addr[i]);
-    load_tile(taddr, kr, vr);
+    bool loaded = false;
     while (i < nslots) {
       const int u = ua + i / P;
       while (s_wpre[s + 1] <= u) ++s;
@@ -777,6 +784,10 @@ void decode_stream_kernel(DecodeArgs a) {
         lim = (!kBf16 || lc / G == m) ? len : 0;
         vlim = len;
       }
+      if (!loaded) {
+        load_tile(taddr, shared, kr, vr);
+        loaded = true;
+      }
       while (i < piece_end) {
         int inext = i + 1;
         if (P > 1) {
@@ -785,11 +796,10 @@ void decode_stream_kernel(DecodeArgs a) {
         }
         // Loads past the run's last tile re-read it (an L2 hit) so that every
         // iteration issues the same loads.
-        const uint32_t naddr =
-            inext < nslots ? (uint32_t)uniform_int((int)s_addr[inext]) : taddr;
+        const uint32_t naddr = inext < nslots ? (uint32_t)uniform_int((int)s_addr[inext]) : taddr;
         const bool bad = taddr == kBadTile;
         process(st * kTile, bad ? 0 : lim, bad ? 0 : vlim, kr, vr,
-                [&] { load_tile(naddr, kr, vr); });
+                [&] { load_tile(naddr, shared, kr, vr); });
         taddr = naddr;
         i = inext;
         ++st;

@@ -130,6 +130,11 @@ pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_head
     return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for dtype %d, head_dim %d, block_size %d, "
                 "group %d (built: f32 head_dim 64, bf16 head_dim 128; block 16 or 32; group 1, "
                 "2, 4 or 8)", (int)c->dtype, (int)c->head_dim, (int)c->block_size, group);
+  // Staged tile addresses (block * tiles per block + tile) keep the top bit
+  // free for a flag.
+  if ((int64_t)c->num_blocks * (c->block_size / 16) > (int64_t{1} << 31) - 16)
+    return fail(PKV_ERR_UNSUPPORTED, "a pool of %d blocks of %d tokens is too large for decode",
+                (int)c->num_blocks, (int)c->block_size);
   const int64_t pt =
       part_tokens > 0 ? std::min<int64_t>(ceil_div64(part_tokens, 16), pkv::kMaxRangeTiles) : 1;
   // Tiles a member can own: its own tiles, or (block 32) the shared tiles of
