@@ -238,8 +238,8 @@ size_t pkv_decode_noalloc_max_workspace(void);
  *   workspace    device scratch of at least pkv_extend_workspace_size()
  *                bytes when the call splits; may be NULL when that size is
  *                0.  Contents need no initialisation and are left undefined.
- *                It holds each partition's max and sum (fp32) and normalised
- *                output (bf16) per query row and head, merged by a second
+ *                It holds each partition's max, sum and normalised output
+ *                (all fp32) per query row and head, merged by a second
  *                kernel in a fixed order.
  * Supported: bf16 caches with head_dim 128, block_size 16 or 32, G in
  * {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.

@@ -447,14 +447,10 @@ void extend_kernel(ExtendArgs a) {
         const int64_t idx =
             ((int64_t)(q0 + j) * a.q_heads + g * G + col % G) * a.num_parts + part;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + idx * kD + 4 * rg;
+        float* po = a.part_o + idx * kD + 4 * rg;
 #pragma unroll
-        for (int db = 0; db < kD / 16; ++db) {
-          bf16x4_t w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[cg][db][i] * inv);
-          *reinterpret_cast<bf16x4_t*>(po + 16 * db) = w;
-        }
+        for (int db = 0; db < kD / 16; ++db)
+          *reinterpret_cast<f32x4_t*>(po + 16 * db) = ot[cg][db] * inv;
         if (rg == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * idx) = float2{m_run[cg], l_tot};
       }
     }
@@ -500,17 +496,17 @@ __global__ __launch_bounds__(64 * kMergeRowsPerWg) void extend_merge_kernel(Exte
   if (j >= n) return;
   const int64_t base = ((int64_t)(q0 + j) * a.q_heads + h) * a.num_parts;
   const float* ml = a.part_ml + 2 * base;
-  const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o) + base * kD + 2 * lane;
+  const float* po = a.part_o + base * kD + 2 * lane;
   float M = -INFINITY;
   for (int p = 0; p < a.num_parts; ++p) M = fmaxf(M, ml[2 * p]);
   float lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int p = 0; p < a.num_parts; ++p) {
     const float m = ml[2 * p];
     const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * p + 1];
-    const uint32_t o2 = *reinterpret_cast<const uint32_t*>(po + (int64_t)p * kD);
+    const float2 o2 = *reinterpret_cast<const float2*>(po + (int64_t)p * kD);
     lsum += w;
-    acc0 = fmaf(w, __uint_as_float(o2 << 16), acc0);
-    acc1 = fmaf(w, __uint_as_float(o2 & 0xffff0000u), acc1);
+    acc0 = fmaf(w, o2.x, acc0);
+    acc1 = fmaf(w, o2.y, acc1);
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   __bf16* out = reinterpret_cast<__bf16*>(a.out) + ((int64_t)(q0 + j) * a.q_heads + h) * kD +

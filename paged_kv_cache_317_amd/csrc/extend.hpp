@@ -28,7 +28,7 @@ struct ExtendArgs {
   int32_t part_tokens;         // keys per partition (a multiple of 64)
   int32_t num_parts;           // partitions per query tile (1: no split)
   float* part_ml;              // split: [T, Hq, P, 2] (max in log2 units, sum)
-  void* part_o;                // split: [T, Hq, P, D] bf16, normalised
+  float* part_o;               // split: [T, Hq, P, D] fp32, normalised
   uint32_t row_bytes;          // one slot: kv_heads * head_dim * element bytes
   uint32_t block_bytes;        // block_size slots
   float scale_log2;            // scale * log2(e)

@@ -362,9 +362,9 @@ pkv_status plan_extend(const pkv_cache_desc* c, int32_t num_seqs, int32_t num_to
   plan->num_parts = (keys + pt - 1) / pt;
   plan->workspace = 0;
   if (plan->num_parts > 1) {
+    // fp32 (max, sum) and fp32 normalised output per row and partition
     const int64_t rows = (int64_t)num_tokens * q_heads * plan->num_parts;
-    plan->workspace = (size_t)(round_up(2 * rows, 4) * sizeof(float) +
-                               rows * c->head_dim * elem_bytes(c->dtype));
+    plan->workspace = (size_t)(round_up(2 * rows, 4) + rows * c->head_dim) * sizeof(float);
   }
   return PKV_OK;
 }

@@ -223,7 +223,8 @@ def test_extend_split_policy_and_workspace_size():
     assert got == max(-(-msl // parts), 1024) and got % 64 == 0
     P = -(-msl // got)
     rows = T * Hq * P
-    assert size(S, T, Hq, maxq, msl, 0) == -(-2 * rows // 4) * 4 * 4 + rows * 128 * 2
+    # fp32 (max, sum) pairs padded to 16 bytes, then the fp32 normalised outputs
+    assert size(S, T, Hq, maxq, msl, 0) == -(-2 * rows // 4) * 4 * 4 + rows * 128 * 4
     # enough units, or short keys: no split, no workspace
     assert part(2, 2048, Hq, 1024, msl, 0) == msl
     assert size(2, 2048, Hq, 1024, msl, 0) == 0
