@@ -84,7 +84,8 @@ def copy_probe(gib, steps, warmup):
 
 DECODE_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_decode.hip",
                   "paged_kv_cache_317_amd/csrc/device_common.hpp",
-                  "paged_kv_cache_317_amd/csrc/decode.hpp"]
+                  "paged_kv_cache_317_amd/csrc/decode.hpp",
+                  "paged_kv_cache_317_amd/csrc/pkv_api.cpp"]   # the run count
 EXTEND_SOURCES = ["paged_kv_cache_317_amd/csrc/attn_extend.hip",
                   "paged_kv_cache_317_amd/csrc/device_common.hpp",
                   "paged_kv_cache_317_amd/csrc/extend.hpp"]

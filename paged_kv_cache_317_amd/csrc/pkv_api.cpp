@@ -99,10 +99,14 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // host sees only max_seq_len, so the run count comes from the largest
 // stream the call can have: enough runs for about kWaveTarget waves, no run
 // shorter than kMinRunTiles tiles on a full-length batch, and no run longer
-// than the kMaxRangeTiles tile slots a workgroup stages in LDS.  With one run
-// the call needs no workspace and no merge.
+// than the kMaxRangeTiles tile slots a workgroup stages in LDS.  A batch too
+// small for kFillWaves waves at that run length still gets that many waves
+// (one partition per run at most): with the chip that empty, a tile costs
+// the latency of its loads, so shorter runs finish sooner than the merge
+// they add costs.  With one run the call needs no workspace and no merge.
 constexpr int64_t kWaveTarget = PKV_DECODE_WAVE_TARGET;
 constexpr int64_t kMinRunTiles = 32;
+constexpr int64_t kFillWaves = 1024;   // 256 CUs, one four-wave workgroup each
 
 struct DecodePlan {
   int64_t part_tiles = 1;
@@ -144,7 +148,8 @@ pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_head
   if (units_bound > INT32_MAX / 2)
     return fail(PKV_ERR_SHAPE, "num_seqs * max_seq_len is too large for one decode call");
   int64_t n = ceil_div64(kWaveTarget, c->kv_heads);
-  n = std::min(n, std::max<int64_t>(1, ceil_div64(units_bound, ceil_div64(kMinRunTiles, pt))));
+  const int64_t fill = std::min(ceil_div64(kFillWaves, c->kv_heads), units_bound);
+  n = std::min(n, std::max({int64_t{1}, ceil_div64(units_bound, ceil_div64(kMinRunTiles, pt)), fill}));
   n = std::max(n, ceil_div64(units_bound, pkv::kMaxRangeTiles / pt));
   n = std::max<int64_t>(1, std::min(n, std::max<int64_t>(units_bound, 1)));
   // From 8 runs on: a multiple of 8, each run on one XCD, odd XCDs' runs

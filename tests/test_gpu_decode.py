@@ -229,6 +229,28 @@ def test_edge_lengths(lens):
             assert torch.count_nonzero(got[s]) == 0
 
 
+@pytest.mark.parametrize("name,L", [("c3_gqa4k_bf16", 1), ("c3_gqa4k_bf16", 777),
+                                    ("c3_gqa4k_bf16", 4000), ("c1_tiny_f32", 100),
+                                    ("c3_gqa4k_bf16", 0)])
+def test_single_run(name, L):
+    """A call whose whole stream is one partition (one sequence within one
+    8192-token partition) runs as one workgroup per kv-head group, with no
+    workspace and no merge: it writes its rows itself, zeros for an empty
+    sequence."""
+    cfg = scaled(get_config(name), num_seqs=1, seq_lens=(max(L, 1),), max_len=max(L, 16))
+    w = generate_host(cfg)
+    d = upload(w)
+    sl = np.array([L], dtype=np.int32)
+    msl = max(L, 16)
+    assert pkv.decode_runs(d["k_cache"], 1, cfg.q_heads, msl, 8192) == 1
+    assert pkv.decode_workspace_size(d["k_cache"], 1, cfg.q_heads, msl, 8192) == 0
+    log(f"single run {name} L={L}")
+    got = _decode(d, w, part_tokens=8192, seq_lens=to_device(sl, None), max_seq_len=msl)
+    compare(got, oracle_decode(w, seq_lens=sl), cfg.dtype)
+    if L == 0:
+        assert torch.count_nonzero(got) == 0
+
+
 @pytest.mark.parametrize("dtype_case", ["bf16", "f32"])
 @pytest.mark.parametrize("nparts", [2, 3, 4, 5, 8, 9, 16, 17])
 def test_partition_lengths_and_merge_counts(dtype_case, nparts):

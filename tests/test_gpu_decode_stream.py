@@ -23,10 +23,13 @@ from helpers import compare, drop_bad_blocks, log, out_to_f64, to_device
 pytestmark = pytest.mark.gpu
 
 # Tiles per sequence 10, 0, 5, 3, 40, 7, 1, 64, 50, 20 (200 in all): with
-# max_seq_len 1024 the call has 24 runs of 9 tiles, so sequence ends land on
-# run boundaries (18, 180), inside runs (10, 15, 58, 65, 66, 130, 200), and
-# sequences sit wholly inside one run (tiles [10, 15), [15, 18), [65, 66)).
+# max_seq_len 1024 and 64 kv heads the call has 24 runs of 9 tiles, so
+# sequence ends land on run boundaries (18, 180), inside runs (10, 15, 58,
+# 65, 66, 130, 200), and sequences sit wholly inside one run (tiles [10, 15),
+# [15, 18), [65, 66)).  With few kv heads the library spreads a batch this
+# small over one partition per run instead; 64 heads keep the runs long.
 STREAM_LENS = (160, 0, 70, 33, 630, 100, 1, 1024, 790, 305)
+STREAM_KV_HEADS = 64
 
 
 def _run_starts(total_units, runs):
@@ -91,7 +94,7 @@ def test_runs_cross_sequence_ends(dtype, part):
     """Runs that end inside a sequence, exactly at a sequence's end, around an
     empty sequence, and sequences wholly inside one run."""
     rng = np.random.default_rng(41)
-    BS, Hkv, G = 16, 2, 4
+    BS, Hkv, G = 16, STREAM_KV_HEADS, 4
     kc, vc, table, q = _batch(rng, STREAM_LENS, BS, Hkv, G, dtype)
     S, max_len = len(STREAM_LENS), 1024
     runs = pkv.decode_runs(to_device(kc, dtype), S, Hkv * G, max_len, part)
@@ -118,7 +121,7 @@ def test_runs_skip_table_entries_outside_the_pool(part):
     sequence, whichever run holds it and however the call splits; other
     sequences are unaffected."""
     rng = np.random.default_rng(42)
-    BS, Hkv, G = 16, 2, 4
+    BS, Hkv, G = 16, STREAM_KV_HEADS, 4
     kc, vc, table, q = _batch(rng, STREAM_LENS, BS, Hkv, G, "bf16")
     NB = kc.shape[0]
     bad = table.copy()
@@ -163,24 +166,25 @@ def _shared_case(rng, G, BS, S, nshared):
     return lens, share
 
 
+@pytest.mark.parametrize("Hkv", [2, STREAM_KV_HEADS])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("BS", [16, 32])
-def test_shared_prefix_groups(G, BS):
+def test_shared_prefix_groups(G, BS, Hkv):
     """Groups of 16 / G sequences sharing 0, 1, 3 or 20 leading blocks (the
     shared blocks are read once per group), a partial last group, members
     ending inside or at the end of the shared blocks; both the library's
-    split and 64-token partitions."""
+    split and 64-token partitions, in runs of one partition (2 kv heads) and
+    in runs of many (64)."""
     rng = np.random.default_rng(1000 + G * 10 + BS)
     gs = 16 // G
     S = 3 * gs + max(1, gs // 2) + (1 if gs == 1 else 0)
     lens, share = _shared_case(rng, G, BS, S, nshared=[20, 3, 0, 1])
-    Hkv = 2
     kc, vc, table, q = _batch(rng, lens, BS, Hkv, G, "bf16", share=share)
     max_len = int(max(lens))
     scale = 0.08
     ref = oracle.decode_attention(q, kc, vc, table, np.array(lens), scale, "bf16")
     for part in (0, 64):
-        log(f"shared G={G} BS={BS} S={S} part={part} lens={lens[:6]}")
+        log(f"shared G={G} BS={BS} Hkv={Hkv} S={S} part={part} lens={lens[:6]}")
         got = _run(kc, vc, table, q, lens, "bf16", scale, max_len, part)
         compare(got, ref, "bf16")
 
@@ -195,7 +199,7 @@ def test_shared_prefix_with_out_of_pool_entry_and_long_groups():
     lens = [130 * 16 + 40, 130 * 16 + 7, 130 * 16, 129 * 16 + 3,
             300, 290, 310, 280]
     share = {0: (4, 130), 4: (4, 12)}
-    kc, vc, table, q = _batch(rng, lens, BS, 2, G, "bf16", share=share)
+    kc, vc, table, q = _batch(rng, lens, BS, STREAM_KV_HEADS, G, "bf16", share=share)
     NB = kc.shape[0]
     table[5, 6] = -1            # member 1 of group 1 holds a bad entry in the shared run
     t2, l2 = drop_bad_blocks(table, np.array(lens), BS, NB)

@@ -66,10 +66,10 @@ def test_noalloc_matches_decode_on_two_calls_in_a_row():
 
 
 def test_noalloc_single_run_and_refusal():
-    # one run: no workspace at all
-    w = generate_host(get_config("c1_tiny_f32"))
+    # one run (a single sequence of one tile): no workspace at all
+    w = generate_host(scaled(get_config("c1_tiny_f32"), num_seqs=1, seq_lens=(13,), max_len=16))
     d = upload(w)
-    assert pkv.decode_runs(d["k_cache"], 4, 8, w.layout.max_seq_len) == 1
+    assert pkv.decode_runs(d["k_cache"], 1, 8, w.layout.max_seq_len) == 1
     out = torch.empty_like(d["q"])
     assert _noalloc(d, w, out) == 0
     torch.cuda.synchronize()
