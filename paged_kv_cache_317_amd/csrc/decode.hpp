@@ -9,7 +9,9 @@ namespace pkv {
 
 // Tiles (16 token positions each) one workgroup's run of the work stream may
 // hold: the run's table entries are staged in LDS, one per tile.
-constexpr int kMaxRangeTiles = 512;
+constexpr int kMaxRangeTiles = 1024;
+// Longest partition a call may ask for, in tiles (8192 positions).
+constexpr int kMaxPartTiles = 512;
 
 struct DecodeArgs {
   const void* q;

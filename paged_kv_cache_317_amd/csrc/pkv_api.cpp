@@ -140,7 +140,7 @@ pkv_status plan_decode(const pkv_cache_desc* c, int32_t num_seqs, int32_t q_head
     return fail(PKV_ERR_UNSUPPORTED, "a pool of %d blocks of %d tokens is too large for decode",
                 (int)c->num_blocks, (int)c->block_size);
   const int64_t pt =
-      part_tokens > 0 ? std::min<int64_t>(ceil_div64(part_tokens, 16), pkv::kMaxRangeTiles) : 1;
+      part_tokens > 0 ? std::min<int64_t>(ceil_div64(part_tokens, 16), pkv::kMaxPartTiles) : 1;
   // Tiles a member can own: its own tiles, or (block 32) the shared tiles of
   // its group, one more at most.
   const int64_t tmax = ceil_div64(max_seq_len, 16) + (c->block_size / 16 - 1);

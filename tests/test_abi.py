@@ -116,12 +116,13 @@ def _decode_workspace(S, Hkv, G, runs, dtype=1, D=128):
 
 @pytest.mark.parametrize("S,Hkv,max_len,req,part,runs", [
     (256, 8, 4096, 0, 16, 256),       # the 4k GQA batch: 2048 waves in 256 runs
-    (16, 8, 131072, 0, 16, 272),      # long contexts: runs capped by the 512 tile slots
-    (16, 8, 131072, 512, 512, 272),   # 512-token partitions (32 tiles): 16 per run at most
+    (16, 8, 131072, 0, 16, 256),      # long contexts: 256 runs of up to 534 tiles
+    (16, 8, 131072, 512, 512, 256),   # 512-token partitions (32 tiles): 17 per run at most
+    (16, 32, 131072, 0, 16, 136),     # 32 kv heads: 128 runs would exceed the 1024 tile slots
     (4, 8, 100, 0, 16, 32),           # 28 tiles at most: one tile per run (fill), 28 -> 32
     (4, 64, 100, 0, 16, 16),          # 64 kv heads fill the chip with 16 runs of 2 tiles
     (1, 8, 16, 0, 16, 1),             # one tile: one run, no workspace
-    (2, 8, 1_000_000, 0, 16, 256),    # 245 runs would do; 256 kept for the waves
+    (2, 8, 1_000_000, 0, 16, 256),    # 123 runs would do; 256 kept for the waves
     (64, 32, 2048, 0, 16, 64),        # 32 kv heads: 64 runs make 2048 waves
     (3, 1, 4000, 100, 112, 112),      # 108 partitions, one per run (fill), rounded to 112
     (10, 64, 1024, 32, 32, 24),       # runs of at least 16 partitions: 20, rounded to 24
@@ -131,7 +132,7 @@ def test_decode_run_choice(S, Hkv, max_len, req, part, runs):
     least 32 tiles on a full-length batch, unless that leaves fewer than
     1024 waves: then up to 1024 waves, one partition per run at most; from
     8 runs on a multiple of 8, odd runs 942/1024 of an even run; the longest
-    run within the 512 tile slots) and the workspace is sized for it."""
+    run within the 1024 tile slots) and the workspace is sized for it."""
     d = _desc(hkv=Hkv)
     L = lib()
     assert L.pkv_decode_partition_tokens(ctypes.byref(d), S, Hkv * 4, max_len, req) == part
@@ -142,7 +143,7 @@ def test_decode_run_choice(S, Hkv, max_len, req, part, runs):
     if got >= 8:
         assert got % 8 == 0
         longest = -(-units_bound * 1024 // ((got // 2) * (1024 + 942)))
-        assert longest * pt <= 512
+        assert longest * pt <= 1024
     ws = L.pkv_decode_workspace_size(ctypes.byref(d), S, Hkv * 4, max_len, req)
     assert ws == _decode_workspace(S, Hkv, 4, got)
 

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import paged_kv_cache_317_amd as pkv
-from workloads import generate_device, generate_host, get_config
+from workloads import generate_device, generate_host, get_config, scaled
 
 from helpers import compare, log, to_device, to_host, upload
 
@@ -66,3 +66,28 @@ def test_full_config_device_generated(name):
     ref = oracle.decode_attention(q, k0, v0, lay.block_table, lay.seq_lens, cfg.scale, cfg.dtype)
     mabs, mrel = compare(out, ref, cfg.dtype)
     log(f"  all {cfg.num_seqs} sequences: max-abs {mabs:.3e} row max-rel {mrel:.3e}")
+
+
+@pytest.mark.parametrize("part", [0, 512])
+def test_long_context_runs_past_512_tiles(part):
+    """The long-context batch with every sequence at its maximum length
+    (131072 positions): the call keeps 256 runs, so a run holds more than
+    512 tiles (the even runs 534 with 16-position partitions, 544 with
+    512-position ones); first and last sequence against the oracle."""
+    cfg = scaled(get_config("c5_long_bf16"), len_range=(131072, 131072), part_tokens=part)
+    w = generate_device(cfg)
+    lay = w.layout
+    runs = pkv.decode_runs(w.k_cache, cfg.num_seqs, cfg.q_heads, lay.max_seq_len, part)
+    log(f"long runs part={part}: runs={runs} pool={lay.num_blocks}")
+    assert runs == 256
+    out = pkv.paged_attn_decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, cfg.scale,
+                                lay.max_seq_len, part_tokens=part)
+    torch.cuda.synchronize()
+    idx = np.array([0, cfg.num_seqs - 1])
+    k0 = to_host(w.k_cache, cfg.dtype)
+    v0 = to_host(w.v_cache, cfg.dtype)
+    q = to_host(w.q, cfg.dtype)[idx]
+    ref = oracle.decode_attention(q, k0, v0, lay.block_table[idx], lay.seq_lens[idx], cfg.scale,
+                                  cfg.dtype)
+    mabs, mrel = compare(out[torch.as_tensor(idx, device=out.device)], ref, cfg.dtype)
+    log(f"  max-abs {mabs:.3e} row max-rel {mrel:.3e}")
