@@ -126,8 +126,11 @@ pkv_status pkv_paged_kv_write(const void* k, const void* v,
  * are widened exactly; the output is rounded to nearest even for bf16).
  *   q            device, [num_seqs, q_heads, head_dim]
  *   k_cache, v_cache  device, read only
- *   block_table  device, int32 [num_seqs, table_width]; entries at or past
- *                ceil(L / block_size) are never read.  Sequences may share
+ *   block_table  device, int32 [num_seqs, table_width], readable in full;
+ *                entries at or past ceil(L / block_size) never address the
+ *                pool (entry 0 of every row is read to find shared
+ *                blocks, whatever L is; any value is allowed there when
+ *                L == 0).  Sequences may share
  *                physical blocks ("Sharing blocks between sequences"): when
  *                consecutive sequences (16 / G of them for bf16 caches) hold
  *                the same leading blocks, those blocks are read once for all
