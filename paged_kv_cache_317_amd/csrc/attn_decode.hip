@@ -367,19 +367,6 @@ void decode_stream_kernel(DecodeArgs a) {
   const int rg = lane >> 4;            // row group: logits rows 4rg..4rg+3
   const int lc = lane & 15;            // K row / matrix column / V chunk
   const int kvgroups = a.kv_heads / a.heads_per_wg;
-  // Workgroup b runs on XCD b % 8.  With a multiple of 8 runs, run r's
-  // kv-head groups are the workgroups r % 8 + 8 * (kvgroups * (r / 8) + i),
-  // all on XCD r % 8; otherwise run r is workgroups r * kvgroups + i.
-  int r, kvg;
-  if (a.num_ranges % 8 == 0) {
-    const int j = blockIdx.x >> 3;
-    r = (blockIdx.x & 7) + 8 * (j / kvgroups);
-    kvg = j % kvgroups;
-  } else {
-    r = blockIdx.x / kvgroups;
-    kvg = blockIdx.x % kvgroups;
-  }
-  const int g = kvg * a.heads_per_wg + wave;                       // kv head
   const int P = a.part_tiles;
 
   // ---- plan (every workgroup computes the same one) ----
@@ -410,10 +397,39 @@ void decode_stream_kernel(DecodeArgs a) {
     }
     if (tid == 0) s_wpre[S] = total;
   }
-  __syncthreads();
+  // Does any group share tiles?  (Every workgroup reaches the same answer.)
+  int any_sh = 0;
+  if constexpr (GS > 1)
+    for (int k = tid; k < ngroups; k += nthr) any_sh |= s_sh[k] > 0 ? 1 : 0;
+  const bool sharing = __syncthreads_or(any_sh) != 0;
   const int W = s_wpre[S];
+
+  // Workgroup b runs on XCD b % 8.  With a multiple of 8 runs, run r's
+  // kv-head groups are the workgroups r % 8 + 8 * (kvgroups * (r / 8) + i),
+  // all on XCD r % 8, and even runs are longer (the odd XCDs gather more
+  // slowly).  When groups share tiles and 2, 4 or 8 kv-head groups split a
+  // run, XCD x takes kv-head group x % kvgroups of every run instead, so
+  // that an XCD's L2 holds the shared blocks of fewer heads; the runs are
+  // then equal.  Otherwise run r is workgroups r * kvgroups + i.
+  const bool by_heads = sharing && a.num_ranges % 8 == 0 && kvgroups > 1 && 8 % kvgroups == 0;
+  int r, kvg;
+  if (by_heads) {
+    const int x = blockIdx.x & 7;
+    kvg = x % kvgroups;
+    r = x / kvgroups + (8 / kvgroups) * (int)(blockIdx.x >> 3);
+  } else if (a.num_ranges % 8 == 0) {
+    const int j = blockIdx.x >> 3;
+    r = (blockIdx.x & 7) + 8 * (j / kvgroups);
+    kvg = j % kvgroups;
+  } else {
+    r = blockIdx.x / kvgroups;
+    kvg = blockIdx.x % kvgroups;
+  }
+  const int g = kvg * a.heads_per_wg + wave;                       // kv head
   RunMap rm;
-  {
+  if (by_heads) {
+    rm.ce = rm.co = max(1, ceil_div(W, a.num_ranges));
+  } else {
     // Even runs hold ce partitions, odd runs co = ceil(ce * odd_q10 / 1024):
     // (N / 2) * (ce + co) >= W covers the stream.
     const int64_t pairs_q10 = (int64_t)(a.num_ranges >> 1) * (1024 + a.odd_q10) +
