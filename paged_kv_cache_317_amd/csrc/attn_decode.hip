@@ -540,8 +540,12 @@ void decode_stream_kernel(DecodeArgs a) {
       for (int j = 0; j < 4; ++j) qv[c][j] = live ? w[j] : 0u;
     }
     col_len = live ? s_len[sq] : 0;
-    int mx = 0;
-    for (int m = 0; m < min(GS, S - s0); ++m) mx = max(mx, s_len[s0 + m]);
+    // The group's longest member: a max over the 16 columns of a row.
+    int mx = col_len;
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+    }
     max_len = uniform_int(mx);
     reset_state();
   };
@@ -706,33 +710,42 @@ void decode_stream_kernel(DecodeArgs a) {
     const int shared_units = ceil_div(shared_of(k), P);
     const int p0 = s_wpre[s0];
     const int64_t slot = (int64_t)r + k;
-    for (int m = 0; m < nm; ++m) {
-      const int s = s0 + m;
-      const Contrib cb(s_wpre[s], s_wpre[s + 1], p0, shared_units, m, rm);
-      if (!cb.has(r)) continue;
-      const bool final_row = cb.count == 1;
-      if constexpr (kBf16) {
-        if (lc / G != m) continue;
-        if (final_row) {
-          // Lane (r, c) owns dims 16dt + 4r .. +3 of column c.
-          const int64_t orow = (int64_t)s * Hq + g * G + lc % G;
-          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-          __bf16* out = reinterpret_cast<__bf16*>(a.out) + orow * D + 4 * rg;
+    if constexpr (kBf16) {
+      // Each lane settles its own column's member (m = c / G): all members
+      // of the group at once.
+      const int m = lc / G;
+      if (m < nm) {
+        const int s = s0 + m;
+        const Contrib cb(s_wpre[s], s_wpre[s + 1], p0, shared_units, m, rm);
+        if (cb.has(r)) {
+          if (cb.count == 1) {
+            // Lane (r, c) owns dims 16dt + 4r .. +3 of column c.
+            const int64_t orow = (int64_t)s * Hq + g * G + lc % G;
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            __bf16* out = reinterpret_cast<__bf16*>(a.out) + orow * D + 4 * rg;
 #pragma unroll
-          for (int dt = 0; dt < kDimTiles; ++dt) {
-            bf16x4_t w;
+            for (int dt = 0; dt < kDimTiles; ++dt) {
+              bf16x4_t w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[dt][i] * inv);
-            *reinterpret_cast<bf16x4_t*>(out + 16 * dt) = w;
+              for (int i = 0; i < 4; ++i) w[i] = (__bf16)(ot[dt][i] * inv);
+              *reinterpret_cast<bf16x4_t*>(out + 16 * dt) = w;
+            }
+          } else {
+            const int64_t prow = slot * rows_per_slot + g * CW + lc;
+            float* po = a.part_o + prow * D + 4 * rg;
+#pragma unroll
+            for (int dt = 0; dt < kDimTiles; ++dt)
+              *reinterpret_cast<f32x4_t*>(po + 16 * dt) = ot[dt];
+            if (rg == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * prow) = float2{m_run, l_tot};
           }
-        } else {
-          const int64_t prow = slot * rows_per_slot + g * CW + lc;
-          float* po = a.part_o + prow * D + 4 * rg;
-#pragma unroll
-          for (int dt = 0; dt < kDimTiles; ++dt) *reinterpret_cast<f32x4_t*>(po + 16 * dt) = ot[dt];
-          if (rg == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * prow) = float2{m_run, l_tot};
         }
-      } else {
+      }
+    } else {
+      for (int m = 0; m < nm; ++m) {
+        const int s = s0 + m;
+        const Contrib cb(s_wpre[s], s_wpre[s + 1], p0, shared_units, m, rm);
+        if (!cb.has(r)) continue;
+        const bool final_row = cb.count == 1;
         // Lanes of row group h % 4 store head h (chunk lc each).
         static_for<G>([&](auto H) {
           constexpr int h = H;
