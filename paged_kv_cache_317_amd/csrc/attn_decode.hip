@@ -252,21 +252,32 @@ __device__ void find_shared_prefixes(const DecodeArgs& a, const int* s_len, cons
   const int64_t MB = a.table_width;
   int* s_cand = scr;                   // group ids of the candidates
   int* s_mis = scr + kBatch;           // first block not shared (so far)
-  int* s_count = scr + 2 * kBatch;
+  int* s_nb = scr + 2 * kBatch;        // fewest blocks of a member, per group
+  int* s_eq = scr + 3 * kBatch;        // every member's block 0 is member 0's
+  int* s_count = scr + 4 * kBatch;
   for (int kb = 0; kb < ngroups; kb += kBatch) {
     if (tid == 0) *s_count = 0;
-    __syncthreads();
     const int kend = min(ngroups, kb + kBatch);
+    for (int k = kb + tid; k < kend; k += nthr) {
+      s_nb[k - kb] = INT_MAX;
+      s_eq[k - kb] = 1;
+    }
+    __syncthreads();
+    // One thread per sequence of the batch's groups.
+    for (int s = kb * GS + tid; s < min(S, kend * GS); s += nthr) {
+      const int k = s / GS;
+      atomicMin(&s_nb[k - kb], ceil_div(s_len[s], BS));
+      if (s % GS != 0 && s_e0[s] != s_e0[k * GS]) s_eq[k - kb] = 0;
+    }
+    __syncthreads();
     for (int k = kb + tid; k < kend; k += nthr) {
       const int s0 = k * GS;
       const int nm = min(GS, S - s0);
-      int nb = INT_MAX;
-      for (int m = 0; m < nm; ++m) nb = min(nb, ceil_div(s_len[s0 + m], BS));
+      const int nb = s_nb[k - kb];
       int shared_blocks = 0;
       if (nm >= 2 && nb >= 1) {
         const int e0 = s_e0[s0];
-        bool eq = e0 >= 0 && e0 < a.num_blocks;
-        for (int m = 1; m < nm; ++m) eq = eq && s_e0[s0 + m] == e0;
+        const bool eq = e0 >= 0 && e0 < a.num_blocks && s_eq[k - kb] != 0;
         if (eq) {
           if (nb == 1) {
             shared_blocks = 1;
@@ -344,7 +355,7 @@ void decode_stream_kernel(DecodeArgs a) {
   constexpr int kKRow = D * 2 + 16;
   constexpr int kKTileBytes = kBf16 ? kTile * kKRow : 16;
   constexpr int kDimTiles = D / 16;
-  static_assert(!kBf16 || kMaxWavesPerWg * kKTileBytes >= 4 * (2 * 256 + 1),
+  static_assert(!kBf16 || kMaxWavesPerWg * kKTileBytes >= 4 * (4 * 256 + 1),
                 "the prologue scratch fits the K tiles");
 
   // Plan of the work stream (dynamic size): clamped lengths [S], prefix of
