@@ -166,7 +166,7 @@ def _shared_case(rng, G, BS, S, nshared):
     return lens, share
 
 
-@pytest.mark.parametrize("Hkv", [2, STREAM_KV_HEADS])
+@pytest.mark.parametrize("Hkv", [2, 16, STREAM_KV_HEADS])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("BS", [16, 32])
 def test_shared_prefix_groups(G, BS, Hkv):
@@ -174,7 +174,8 @@ def test_shared_prefix_groups(G, BS, Hkv):
     shared blocks are read once per group), a partial last group, members
     ending inside or at the end of the shared blocks; both the library's
     split and 64-token partitions, in runs of one partition (2 kv heads) and
-    in runs of many (64)."""
+    in runs of many (64), and with 16 kv heads, whose four kv-head groups
+    then go to the XCDs one group per XCD (equal runs)."""
     rng = np.random.default_rng(1000 + G * 10 + BS)
     gs = 16 // G
     S = 3 * gs + max(1, gs // 2) + (1 if gs == 1 else 0)
