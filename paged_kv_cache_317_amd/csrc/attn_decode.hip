@@ -57,10 +57,11 @@
 // f32 caches use v_mfma_f32_16x16x4_f32 for the logits and fp32 FMAs for P.V
 // (each lane owns one 16-byte chunk of the value rows of four tokens).
 //
-// Loads: a K or V tile is four 16-byte non-temporal loads per lane, each
-// instruction covering 4 whole 256-byte rows.  bf16 K is re-laid out through
-// a padded LDS tile into the operand layout.  Every cached byte a group needs
-// is read from HBM once per call and kv head.
+// Loads: a K or V tile is four 16-byte loads per lane, each instruction
+// covering 4 whole 256-byte rows: non-temporal for a member's own tiles
+// (read once per call and kv head), through the caches for shared tiles
+// (other groups may read the same blocks).  bf16 K is re-laid out through a
+// padded LDS tile into the operand layout.
 #include <climits>
 #include <utility>
 
