@@ -164,7 +164,7 @@ pkv_status pkv_paged_kv_write(const void* k, const void* v,
  * differ in the last bits between batches that split a sequence's work
  * differently (other lengths, other sharing), within the fp32 accumulation.
  * Supported: f32 with head_dim 64, bf16 with head_dim 128; block_size 16 or
- * 32; G in {1, 2, 4, 8}; num_seqs up to about 14000 (PKV_ERR_UNSUPPORTED
+ * 32; G in {1, 2, 4, 8}; num_seqs up to about 11000-14000, by G (PKV_ERR_UNSUPPORTED
  * beyond).
  */
 pkv_status pkv_paged_attn_decode(const void* q, const void* k_cache,

@@ -173,6 +173,16 @@ def test_decode_too_many_sequences_for_one_call():
     assert "sequences" in lib().pkv_last_error().decode()
 
 
+def test_decode_sequence_limit_is_the_plan_lds():
+    """Every workgroup plans in LDS: lengths [S], stream prefix [S + 1] and
+    (bf16) shared tiles per group of 16 / G, 112 KB at most.  With G = 4 that
+    is (2 S + 1 + ceil(S / 4)) * 4 <= 114688: 12742 sequences, not 12743."""
+    d = _desc()
+    L = lib()
+    assert L.pkv_decode_runs(ctypes.byref(d), 12742, 32, 100, 0) > 0
+    assert L.pkv_decode_runs(ctypes.byref(d), 12743, 32, 100, 0) == 0
+
+
 def _extend(desc, S=2, T=40, Hq=32, maxq=20, scale=0.1, q=1 << 12, kc=1 << 12, vc=1 << 12,
             table=1 << 12, lens=1 << 12, qs=1 << 12, out=1 << 12, width=8, msl=128, part=0,
             ws=None, ws_bytes=0):

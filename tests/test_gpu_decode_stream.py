@@ -234,3 +234,25 @@ def test_shared_and_private_layouts_agree():
     compare(a, ref, "bf16")
     compare(b, ref, "bf16")
     assert np.abs(out_to_f64(a) - out_to_f64(b)).max() <= 2e-2
+
+
+def test_many_short_sequences_plan_past_48k_lds():
+    """12000 short sequences (lengths 0..48, some sharing their first block
+    in groups of four): every workgroup's plan takes about 108 KB of LDS, past
+    the 48 KB a launch gets by default.  Sampled rows against the oracle,
+    empty sequences give zero rows."""
+    rng = np.random.default_rng(12000)
+    S, BS, Hkv, G = 12000, 16, 2, 4
+    lens = rng.integers(0, 49, size=S)
+    lens[::97] = 0
+    share = {s0: (4, 1) for s0 in range(0, S, 40) if min(lens[s0:s0 + 4]) >= 16}
+    kc, vc, table, q = _batch(rng, lens, BS, Hkv, G, "bf16", share=share)
+    scale = 0.1
+    log(f"many short sequences S={S} groups sharing={len(share)}")
+    got = _run(kc, vc, table, q, lens, "bf16", scale, 48)
+    idx = np.sort(rng.choice(S, size=300, replace=False))
+    idx = np.union1d(idx, np.array(sorted(share)[:20]))
+    ref = oracle.decode_attention(q[idx], kc, vc, table[idx], lens[idx], scale, "bf16")
+    compare(got[torch.as_tensor(idx, device=got.device)], ref, "bf16")
+    zero = np.flatnonzero(lens == 0)
+    assert torch.count_nonzero(got[torch.as_tensor(zero, device=got.device)]) == 0
