@@ -331,9 +331,11 @@ __device__ void find_shared_prefixes(const DecodeArgs& a, const int* s_len, cons
   }
 }
 
-// Occupancy request: waves per SIMD the register allocation must allow.
+// Occupancy request: waves per SIMD the register allocation must allow.  The
+// launches put about two waves on each SIMD; with room for more than 128
+// registers the bf16 instantiations take 131-134 and spill nothing.
 #ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 4
+#define PKV_DECODE_WAVES_PER_EU 2
 #endif
 template <typename T, int D, int BS, int G>
 __global__ __launch_bounds__(64 * kMaxWavesPerWg)
