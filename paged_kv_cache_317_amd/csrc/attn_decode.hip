@@ -296,28 +296,40 @@ __device__ void find_shared_prefixes(const DecodeArgs& a, const int* s_len, cons
     for (int j0 = 1; ncand > 0; j0 += kSpan) {
       const int npairs = ncand * kSpan;
       for (int base = 0; base < npairs; base += nthr * kPairs) {
-        int e[kPairs][GS];
-        int jv[kPairs], cv[kPairs], nmv[kPairs];
+        // Every pair's candidate first (the LDS reads issue together), then
+        // every member's entry of every pair as plain loads from indices
+        // clamped into the table (a pair past the round or past a member
+        // reads an entry it then ignores), so that no load waits on a branch.
+        int jv[kPairs], cv[kPairs], nmv[kPairs], kv[kPairs], misv[kPairs];
+        const int32_t* rp[kPairs];
 #pragma unroll
         for (int u = 0; u < kPairs; ++u) {
           const int t = base + u * nthr + tid;
-          const int c = min(t / kSpan, ncand - 1);
-          const int j = j0 + t % kSpan;
-          const int s0 = s_cand[c] * GS;
-          const int nm = min(GS, S - s0);
-          const bool act = t < npairs && j < s_mis[c];
-#pragma unroll
-          for (int m = 0; m < GS; ++m)
-            e[u][m] = (act && m < nm) ? a.block_table[(s0 + m) * MB + j] : 0;
-          jv[u] = act ? j : INT_MAX;
-          cv[u] = c;
-          nmv[u] = nm;
+          cv[u] = min(t / kSpan, ncand - 1);
+          kv[u] = s_cand[cv[u]];
+          misv[u] = s_mis[cv[u]];
         }
+        // Keep the LDS reads above together: one wait for all of them.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+          const int t = base + u * nthr + tid;
+          const int j = j0 + t % kSpan;
+          const int s0 = kv[u] * GS;
+          nmv[u] = min(GS, S - s0);
+          jv[u] = ((t < npairs) & (j < misv[u])) ? j : INT_MAX;
+          rp[u] = a.block_table + (int64_t)s0 * MB + min(j, (int)MB - 1);
+        }
+        int e[kPairs][GS];
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u)
+#pragma unroll
+          for (int m = 0; m < GS; ++m) e[u][m] = rp[u][(int64_t)min(m, nmv[u] - 1) * MB];
 #pragma unroll
         for (int u = 0; u < kPairs; ++u) {
           bool same = e[u][0] >= 0 && e[u][0] < a.num_blocks;
 #pragma unroll
-          for (int m = 1; m < GS; ++m) same = same && (m >= nmv[u] || e[u][m] == e[u][0]);
+          for (int m = 1; m < GS; ++m) same = same && e[u][m] == e[u][0];
           if (jv[u] != INT_MAX && !same) atomicMin(&s_mis[cv[u]], jv[u]);
         }
       }
