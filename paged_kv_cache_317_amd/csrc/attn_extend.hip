@@ -100,6 +100,19 @@ __device__ __forceinline__ bf16x4_t tr_read(const char* lds, int byte_off) {
 // the kernel's speed.
 __device__ __forceinline__ int chunk_swizzle(int r) { return (r & 15) ^ ((r >> 2) & 3); }
 
+// Sequences a workgroup ranks by their work to order the units.
+constexpr int kRankSeqs = 512;
+
+// Causal work of a sequence in key visits: n new tokens after ctx cached
+// positions see n * ctx + n (n + 1) / 2 keys (n and ctx as the kernel clamps
+// them; only the order of these values is used).
+__device__ __forceinline__ long long causal_work(const ExtendArgs& a, int q0, int n_raw, int L) {
+  if (q0 < 0) return 0;
+  const long long n = max(min(min(n_raw, a.max_query_len), a.num_tokens - q0), 0);
+  const long long ctx = max(min(L, a.max_seq_len) - n_raw, 0);
+  return n * ctx + n * (n + 1) / 2;
+}
+
 template <int BS, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PKV_EXTEND_WAVES_PER_EU)))
 void extend_kernel(ExtendArgs a) {
@@ -117,6 +130,9 @@ void extend_kernel(ExtendArgs a) {
   char* const s_k[2] = {s_k0, s_k1};
   char* const s_v[2] = {s_v0, s_v1};
   __shared__ int s_first_bad;
+  __shared__ long long s_work[kRankSeqs];
+  __shared__ int s_seq[kRankSeqs][3];    // query_start, new tokens, length
+  __shared__ int s_ranked;
 
   // (sequence, kv head) pairs go round-robin over the XCDs (workgroup b runs
   // on XCD b mod 8); on its XCD a pair's query tiles are consecutive, so they
@@ -132,11 +148,48 @@ void extend_kernel(ExtendArgs a) {
   const int part = li / a.q_tiles;
   const int qt = a.q_tiles - 1 - li % a.q_tiles;     // later (longer) query tiles first
   const int g = pair % a.kv_heads;
-  const int s = pair / a.kv_heads;
-  if (s >= a.num_seqs) return;
+  const int rank = pair / a.kv_heads;
+  if (rank >= a.num_seqs) return;                  // uniform over the workgroup
+  // Longest sequences first: pair p of the order above is kv head
+  // p % kv_heads of the sequence ranked p / kv_heads by causal work
+  // (descending; ties by index), so that on every XCD the units that take
+  // longest start first and the last ones to finish are short.  Every
+  // workgroup ranks the sequences itself (batches of up to kRankSeqs
+  // sequences; larger ones keep the order of the batch), from one round of
+  // loads that also gives its own sequence's start, new tokens and length.
+  int s = rank;
+  int q0, n_raw, L;
+  if (a.num_seqs > 1 && a.num_seqs <= kRankSeqs) {
+    for (int i = threadIdx.x; i < a.num_seqs; i += kThreads) {
+      const int qa = a.query_start[i];
+      const int nr = a.query_start[i + 1] - qa;
+      const int len = a.seq_lens[i];
+      s_seq[i][0] = qa;
+      s_seq[i][1] = nr;
+      s_seq[i][2] = len;
+      s_work[i] = causal_work(a, qa, nr, len);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.num_seqs; i += kThreads) {
+      const long long wi = s_work[i];
+      int r = 0;
+      for (int j = 0; j < a.num_seqs; ++j) {
+        const long long wj = s_work[j];
+        r += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
+      }
+      if (r == rank) s_ranked = i;
+    }
+    __syncthreads();
+    s = s_ranked;
+    q0 = s_seq[s][0];
+    n_raw = s_seq[s][1];
+    L = s_seq[s][2];
+  } else {
+    q0 = a.query_start[s];
+    n_raw = a.query_start[s + 1] - q0;
+    L = a.seq_lens[s];
+  }
 
-  const int q0 = a.query_start[s];
-  const int n_raw = a.query_start[s + 1] - q0;
   // Rows outside [0, num_tokens) are never read or written, whatever
   // query_start holds.
   if (q0 < 0) return;
@@ -144,7 +197,6 @@ void extend_kernel(ExtendArgs a) {
   const int j0 = qt * kTokens;
   if (j0 >= n) return;
   const int j1 = min(j0 + kTokens, n);
-  const int L = a.seq_lens[s];
   const int ctx = L - n_raw;                       // position of query 0
 
   // Keys this workgroup may read: below every query's position + 1 and the
