@@ -114,3 +114,35 @@ def test_extend_random_shapes(seed):
     torch.cuda.synchronize()
     ref = oracle.extend_attention(q, kc, vc, table, lens, qs, scale, "bf16")
     compare(out, ref, "bf16")
+
+
+@pytest.mark.parametrize("S,ties", [(511, False), (512, False), (513, False), (300, True)])
+def test_extend_many_sequences_in_any_unit_order(S, ties):
+    """The extend kernel orders its units by each sequence's work when the
+    batch has at most 512 sequences (every workgroup ranks them) and keeps the
+    batch order beyond: batches just below, at and above that size, and one
+    whose sequences all have the same work (the ranking falls back on the
+    sequence index), every output row against the oracle.  Short sequences
+    (0-40 cached, 0-5 new tokens), so that the oracle stays quick."""
+    rng = np.random.default_rng(7000 + S)
+    BS, Hkv, G = 16, 2, 4
+    if ties:
+        ctx = np.full(S, 23)
+        new = np.full(S, 3)
+    else:
+        ctx = rng.integers(0, 41, size=S)
+        new = rng.integers(0, 6, size=S)
+        new[0] = 0
+    lens = ctx + new
+    kc, vc, table = _pool(rng, lens, BS, Hkv, 128, "bf16", 7)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    T = int(qs[-1])
+    q = _values(rng, (T, Hkv * G, 128), "bf16")
+    scale = 0.09
+    log(f"extend order: S={S} T={T} ties={ties}")
+    out = pkv.paged_attn_extend(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
+                                to_device(table, None), to_device(lens.astype(np.int32), None),
+                                to_device(qs, None), scale, int(new.max()), int(lens.max()))
+    torch.cuda.synchronize()
+    ref = oracle.extend_attention(q, kc, vc, table, lens, qs, scale, "bf16")
+    compare(out, ref, "bf16")
