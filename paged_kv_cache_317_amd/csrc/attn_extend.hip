@@ -100,8 +100,10 @@ __device__ __forceinline__ bf16x4_t tr_read(const char* lds, int byte_off) {
 // the kernel's speed.
 __device__ __forceinline__ int chunk_swizzle(int r) { return (r & 15) ^ ((r >> 2) & 3); }
 
-// Sequences a workgroup ranks by their work to order the units.
-constexpr int kRankSeqs = 512;
+// Sequences a workgroup ranks by their work to order the units (each thread
+// ranks one sequence against all of them, so the cost grows with the square
+// of this bound; larger batches have many units and keep their order).
+constexpr int kRankSeqs = 64;
 
 // Causal work of a sequence in key visits: n new tokens after ctx cached
 // positions see n * ctx + n (n + 1) / 2 keys (n and ctx as the kernel clamps

@@ -116,14 +116,16 @@ def test_extend_random_shapes(seed):
     compare(out, ref, "bf16")
 
 
-@pytest.mark.parametrize("S,ties", [(511, False), (512, False), (513, False), (300, True)])
+@pytest.mark.parametrize("S,ties", [(63, False), (64, False), (65, False), (513, False),
+                                    (60, True)])
 def test_extend_many_sequences_in_any_unit_order(S, ties):
     """The extend kernel orders its units by each sequence's work when the
-    batch has at most 512 sequences (every workgroup ranks them) and keeps the
-    batch order beyond: batches just below, at and above that size, and one
-    whose sequences all have the same work (the ranking falls back on the
-    sequence index), every output row against the oracle.  Short sequences
-    (0-40 cached, 0-5 new tokens), so that the oracle stays quick."""
+    batch has at most 64 sequences (every workgroup ranks them) and keeps the
+    batch order beyond: batches just below, at and above that size, a large
+    one, and one whose sequences all have the same work (the ranking falls
+    back on the sequence index), every output row against the oracle.  Short
+    sequences (0-40 cached, 0-5 new tokens), so that the oracle stays
+    quick."""
     rng = np.random.default_rng(7000 + S)
     BS, Hkv, G = 16, 2, 4
     if ties:
