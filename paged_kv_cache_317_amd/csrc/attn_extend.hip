@@ -105,12 +105,21 @@ __device__ __forceinline__ int chunk_swizzle(int r) { return (r & 15) ^ ((r >> 2
 // of this bound; larger batches have many units and keep their order).
 constexpr int kRankSeqs = 64;
 
+// (sequence, kv head) pairs an XCD orders by their live units (below).
+constexpr int kOrderPairs = 64;
+
+// New tokens of a sequence the kernel computes: its query rows clamped to
+// max_query_len and to the packed rows; none when query_start is negative.
+__device__ __forceinline__ int live_tokens(const ExtendArgs& a, int q0, int n_raw) {
+  if (q0 < 0) return 0;
+  return max(min(min(n_raw, a.max_query_len), a.num_tokens - q0), 0);
+}
+
 // Causal work of a sequence in key visits: n new tokens after ctx cached
 // positions see n * ctx + n (n + 1) / 2 keys (n and ctx as the kernel clamps
 // them; only the order of these values is used).
 __device__ __forceinline__ long long causal_work(const ExtendArgs& a, int q0, int n_raw, int L) {
-  if (q0 < 0) return 0;
-  const long long n = max(min(min(n_raw, a.max_query_len), a.num_tokens - q0), 0);
+  const long long n = live_tokens(a, q0, n_raw);
   const long long ctx = max(min(L, a.max_seq_len) - n_raw, 0);
   return n * ctx + n * (n + 1) / 2;
 }
@@ -134,34 +143,41 @@ void extend_kernel(ExtendArgs a) {
   __shared__ int s_first_bad;
   __shared__ long long s_work[kRankSeqs];
   __shared__ int s_seq[kRankSeqs][3];    // query_start, new tokens, length
-  __shared__ int s_ranked;
+  __shared__ int s_order[kRankSeqs];     // sequence of each rank
+  __shared__ int s_units[kOrderPairs];   // live units of this XCD's pairs
+  __shared__ int s_pick[2];              // this unit's pair slot, index in the pair
 
   // (sequence, kv head) pairs go round-robin over the XCDs (workgroup b runs
   // on XCD b mod 8); on its XCD a pair's query tiles are consecutive, so they
   // run side by side and read the pair's keys and values through one L2.
   // A split call (num_parts > 1) also cuts each query tile's keys into
   // partitions of part_tokens; the query tiles of one partition are adjacent.
+  // Later (longer) query tiles come first.  The grid has q_tiles * num_parts
+  // slots per pair, q_tiles counted from max_query_len.
   const int unit = (int)blockIdx.x;
   const int xcd = unit % 8;
   const int local = unit / 8;
   const int per_pair = a.q_tiles * a.num_parts;
-  const int pair = (local / per_pair) * 8 + xcd;
-  const int li = local % per_pair;
-  const int part = li / a.q_tiles;
-  const int qt = a.q_tiles - 1 - li % a.q_tiles;     // later (longer) query tiles first
-  const int g = pair % a.kv_heads;
-  const int rank = pair / a.kv_heads;
-  if (rank >= a.num_seqs) return;                  // uniform over the workgroup
-  // Longest sequences first: pair p of the order above is kv head
-  // p % kv_heads of the sequence ranked p / kv_heads by causal work
-  // (descending; ties by index), so that on every XCD the units that take
-  // longest start first and the last ones to finish are short.  Every
-  // workgroup ranks the sequences itself (batches of up to kRankSeqs
-  // sequences; larger ones keep the order of the batch), from one round of
-  // loads that also gives its own sequence's start, new tokens and length.
-  int s = rank;
-  int q0, n_raw, L;
+  int pair = (local / per_pair) * 8 + xcd;
+  int li = local % per_pair;
+  int qtiles = a.q_tiles;
+  // Longest sequences first: pair p of the order is kv head p % kv_heads of
+  // the sequence ranked p / kv_heads by causal work (descending; ties by
+  // index), so that on every XCD the units that take longest start first and
+  // the last ones to finish are short.  Every workgroup ranks the sequences
+  // itself (batches of up to kRankSeqs sequences; larger ones keep the order
+  // of the batch), from one round of loads that also gives its own
+  // sequence's start, new tokens and length.  When the XCD has at most
+  // kOrderPairs pairs, its slots also skip the query tiles a sequence does
+  // not have (fewer new tokens than max_query_len): each pair takes only its
+  // live units, one after another, and the empty slots move to the end of the
+  // grid, where they return at once instead of sitting between two pairs.
+  int s, q0, n_raw, L;
   if (a.num_seqs > 1 && a.num_seqs <= kRankSeqs) {
+    const int npairs = a.num_seqs * a.kv_heads;
+    const int nx = npairs > xcd ? (npairs - xcd + 7) / 8 : 0;   // pairs xcd + 8 k
+    const bool compact = nx <= kOrderPairs;
+    if (!compact && pair >= npairs) return;          // uniform over the workgroup
     for (int i = threadIdx.x; i < a.num_seqs; i += kThreads) {
       const int qa = a.query_start[i];
       const int nr = a.query_start[i + 1] - qa;
@@ -171,6 +187,7 @@ void extend_kernel(ExtendArgs a) {
       s_seq[i][2] = len;
       s_work[i] = causal_work(a, qa, nr, len);
     }
+    if (threadIdx.x == 0) s_pick[0] = -1;
     __syncthreads();
     for (int i = threadIdx.x; i < a.num_seqs; i += kThreads) {
       const long long wi = s_work[i];
@@ -179,23 +196,49 @@ void extend_kernel(ExtendArgs a) {
         const long long wj = s_work[j];
         r += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
       }
-      if (r == rank) s_ranked = i;
+      s_order[r] = i;
     }
     __syncthreads();
-    s = s_ranked;
+    if (compact) {
+      for (int k = threadIdx.x; k < nx; k += kThreads) {
+        const int sq = s_order[(8 * k + xcd) / a.kv_heads];
+        const int nl = live_tokens(a, s_seq[sq][0], s_seq[sq][1]);
+        s_units[k] = (nl + kTokens - 1) / kTokens * a.num_parts;
+      }
+      __syncthreads();
+      for (int k = threadIdx.x; k < nx; k += kThreads) {
+        int before = 0;
+        for (int k2 = 0; k2 < k; ++k2) before += s_units[k2];
+        if (local >= before && local < before + s_units[k]) {
+          s_pick[0] = k;
+          s_pick[1] = local - before;
+        }
+      }
+      __syncthreads();
+      if (s_pick[0] < 0) return;                     // past this XCD's live units
+      pair = 8 * s_pick[0] + xcd;
+      li = s_pick[1];
+      qtiles = s_units[s_pick[0]] / a.num_parts;
+    }
+    s = s_order[pair / a.kv_heads];
     q0 = s_seq[s][0];
     n_raw = s_seq[s][1];
     L = s_seq[s][2];
   } else {
+    s = pair / a.kv_heads;
+    if (s >= a.num_seqs) return;                     // uniform over the workgroup
     q0 = a.query_start[s];
     n_raw = a.query_start[s + 1] - q0;
     L = a.seq_lens[s];
   }
+  const int g = pair % a.kv_heads;
+  const int part = li / qtiles;
+  const int qt = qtiles - 1 - li % qtiles;
 
   // Rows outside [0, num_tokens) are never read or written, whatever
   // query_start holds.
   if (q0 < 0) return;
-  const int n = min(min(n_raw, a.max_query_len), a.num_tokens - q0);
+  const int n = live_tokens(a, q0, n_raw);
   const int j0 = qt * kTokens;
   if (j0 >= n) return;
   const int j1 = min(j0 + kTokens, n);

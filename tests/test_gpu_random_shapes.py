@@ -116,6 +116,43 @@ def test_extend_random_shapes(seed):
     compare(out, ref, "bf16")
 
 
+@pytest.mark.parametrize("S,Hkv,G,new_hi,part", [
+    (12, 8, 8, 200, 0),      # up to 7 query tiles per sequence, some sequences without any
+    (12, 8, 8, 200, 128),    # the same split into 128-key partitions
+    (64, 8, 2, 300, 0),      # 64 (sequence, kv head) pairs per XCD: the most that are packed
+    (40, 16, 1, 300, 0),     # 80 pairs per XCD: the grid keeps its empty slots
+    (43, 12, 1, 100, 0),     # 516 pairs: XCDs 0-3 keep their empty slots, 4-7 pack
+])
+def test_extend_units_of_uneven_query_tiles(S, Hkv, G, new_hi, part):
+    """Sequences with different numbers of new tokens have different numbers
+    of query tiles, while the grid has max_query_len's worth for each.  In
+    batches of up to 64 sequences whose XCDs hold at most 64 (sequence, kv
+    head) pairs each, every workgroup maps its slot onto the live query tiles
+    of its XCD's pairs, the empty slots last; otherwise the slots keep their
+    fixed places.  Both, on the same XCD mix and split, every output row
+    against the oracle."""
+    rng = np.random.default_rng(7500 + S + Hkv + part)
+    BS = 16
+    ctx = rng.integers(0, 120, size=S)
+    new = rng.integers(0, new_hi + 1, size=S)
+    new[rng.integers(0, S, size=max(1, S // 8))] = 0
+    new[rng.integers(0, S)] = new_hi
+    lens = ctx + new
+    kc, vc, table = _pool(rng, lens, BS, Hkv, 128, "bf16", 9)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    T = int(qs[-1])
+    q = _values(rng, (T, Hkv * G, 128), "bf16")
+    scale = 0.09
+    log(f"extend uneven query tiles: S={S} Hkv={Hkv} G={G} T={T} part={part}")
+    out = pkv.paged_attn_extend(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
+                                to_device(table, None), to_device(lens.astype(np.int32), None),
+                                to_device(qs, None), scale, int(new.max()), int(lens.max()),
+                                part_tokens=part)
+    torch.cuda.synchronize()
+    ref = oracle.extend_attention(q, kc, vc, table, lens, qs, scale, "bf16")
+    compare(out, ref, "bf16")
+
+
 @pytest.mark.parametrize("S,ties", [(63, False), (64, False), (65, False), (513, False),
                                     (60, True)])
 def test_extend_many_sequences_in_any_unit_order(S, ties):
