@@ -574,14 +574,18 @@ void extend_kernel(ExtendArgs a) {
   }
 }
 
-// Merge of a split call: one wave per (query row, head) of every computed
-// row; M = max_p m_p, w_p = 2^(m_p - M) l_p, out = sum_p w_p (o/l)_p /
-// sum_p w_p, in a fixed order.  Lane i owns output elements 2i, 2i + 1.
-constexpr int kMergeRowsPerWg = 4;
+// Merge of a split call: 32 lanes per (query row, head) of every computed
+// row, lane i owning output elements 4i .. 4i + 3.  The partitions are folded
+// in order with the online rescaling the kernel applies per tile: M the
+// running max, each state weighted by 2^(m_p - M) l_p and the running sums
+// rescaled when M moves; out = sum / weight.  Every load of a row is
+// independent of the others, so a row costs one round trip.
+constexpr int kMergeLanes = 32;
+constexpr int kMergeRowsPerWg = 8;
 
-__global__ __launch_bounds__(64 * kMergeRowsPerWg) void extend_merge_kernel(ExtendArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t u = (int64_t)blockIdx.x * kMergeRowsPerWg + (threadIdx.x >> 6);
+__global__ __launch_bounds__(kMergeLanes * kMergeRowsPerWg) void extend_merge_kernel(ExtendArgs a) {
+  const int sub = threadIdx.x % kMergeLanes;
+  const int64_t u = (int64_t)blockIdx.x * kMergeRowsPerWg + threadIdx.x / kMergeLanes;
   const int h = (int)(u % a.q_heads);
   const int64_t rest = u / a.q_heads;
   const int j = (int)(rest % a.max_query_len);
@@ -589,27 +593,33 @@ __global__ __launch_bounds__(64 * kMergeRowsPerWg) void extend_merge_kernel(Exte
   if (s >= a.num_seqs) return;
   const int q0 = a.query_start[s];
   if (q0 < 0) return;
-  const int n = min(min(a.query_start[s + 1] - q0, a.max_query_len), a.num_tokens - q0);
+  const int n = live_tokens(a, q0, a.query_start[s + 1] - q0);
   if (j >= n) return;
   const int64_t base = ((int64_t)(q0 + j) * a.q_heads + h) * a.num_parts;
   const float* ml = a.part_ml + 2 * base;
-  const float* po = a.part_o + base * kD + 2 * lane;
-  float M = -INFINITY;
-  for (int p = 0; p < a.num_parts; ++p) M = fmaxf(M, ml[2 * p]);
-  float lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
+  const float* po = a.part_o + base * kD + 4 * sub;
+  float M = -INFINITY, lsum = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < a.num_parts; ++p) {
-    const float m = ml[2 * p];
-    const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * p + 1];
-    const float2 o2 = *reinterpret_cast<const float2*>(po + (int64_t)p * kD);
+    const float2 st = *reinterpret_cast<const float2*>(ml + 2 * p);
+    const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(po + (int64_t)p * kD);
+    if (st.x == -INFINITY) continue;              // no key of this partition for the row
+    if (st.x > M) {
+      const float c = __builtin_amdgcn_exp2f(M - st.x);   // 0 while M is -inf
+      lsum *= c;
+      acc *= c;
+      M = st.x;
+    }
+    const float w = __builtin_amdgcn_exp2f(st.x - M) * st.y;
     lsum += w;
-    acc0 = fmaf(w, o2.x, acc0);
-    acc1 = fmaf(w, o2.y, acc1);
+    acc += w * o4;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  __bf16* out = reinterpret_cast<__bf16*>(a.out) + ((int64_t)(q0 + j) * a.q_heads + h) * kD +
-                2 * lane;
-  out[0] = (__bf16)(acc0 * inv);
-  out[1] = (__bf16)(acc1 * inv);
+  bf16x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(a.out) +
+                               ((int64_t)(q0 + j) * a.q_heads + h) * kD + 4 * sub) = r;
 }
 
 template <int BS, int G>
@@ -623,7 +633,7 @@ hipError_t launch_one(const ExtendArgs& a, hipStream_t stream) {
   if (err != hipSuccess || a.num_parts == 1) return err;
   const int64_t rows = (int64_t)a.num_seqs * a.max_query_len * a.q_heads;
   hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)((rows + kMergeRowsPerWg - 1) / kMergeRowsPerWg)),
-                     dim3(64 * kMergeRowsPerWg), 0, stream, a);
+                     dim3(kMergeLanes * kMergeRowsPerWg), 0, stream, a);
   return hipGetLastError();
 }
 
