@@ -99,6 +99,8 @@ PROFILES = {
     "c4_prefix_bf16": ("paged_attn_decode_c4_prefix_bf16.md", DECODE_SOURCES),
     "x3_extend_bf16": ("paged_attn_extend_x3_extend_bf16.md", EXTEND_SOURCES),
     "x6_long_extend_bf16": ("paged_attn_extend_x6_long_extend_bf16.md", EXTEND_SOURCES),
+    "x2_prefill_bf16": ("paged_attn_extend_x2_prefill_bf16.md", EXTEND_SOURCES),
+    "x4_extend_g8_bs32_bf16": ("paged_attn_extend_x4_extend_g8_bs32_bf16.md", EXTEND_SOURCES),
 }
 
 
