@@ -115,6 +115,16 @@ __device__ __forceinline__ int live_tokens(const ExtendArgs& a, int q0, int n_ra
   return max(min(min(n_raw, a.max_query_len), a.num_tokens - q0), 0);
 }
 
+// Keys a query tile may read, before the scan for table entries outside the
+// pool: below its last query's position + 1 (ctx + j1) and the sequence's
+// bounds.  In a split call a tile whose bound fits the first partition is
+// complete in that partition's workgroup, which stores its rows itself; the
+// merge leaves them alone.
+__device__ __forceinline__ int tile_key_bound(const ExtendArgs& a, int L, int ctx, int j1, int BS) {
+  const int kv_end = max(min(min(L, a.max_seq_len), a.table_width * BS), 0);
+  return max(min(ctx + j1, kv_end), 0);
+}
+
 // Causal work of a sequence in key visits: n new tokens after ctx cached
 // positions see n * ctx + n (n + 1) / 2 keys (n and ctx as the kernel clamps
 // them; only the order of these values is used).
@@ -248,7 +258,9 @@ void extend_kernel(ExtendArgs a) {
   // sequence length; a table entry outside the pool ends the sequence at
   // that block.
   int kv_end = max(min(min(L, a.max_seq_len), a.table_width * BS), 0);
-  int kv_hi = max(min(ctx + j1, kv_end), 0);
+  int kv_hi = tile_key_bound(a, L, ctx, j1, BS);
+  const bool direct = a.num_parts > 1 && kv_hi <= a.part_tokens;
+  if (direct && part > 0) return;                  // uniform: its keys are all in partition 0
   const int nblk = (kv_hi + BS - 1) / BS;
   const int32_t* trow = a.block_table + (int64_t)s * a.table_width;
   if (threadIdx.x == 0) s_first_bad = nblk;
@@ -530,7 +542,7 @@ void extend_kernel(ExtendArgs a) {
     }
   }
 
-  if (a.num_parts > 1) {
+  if (a.num_parts > 1 && !direct) {
     // Split: each valid column's state for this partition -- running max
     // (log2 units) and sum in fp32, the output normalised by the sum in
     // bf16 -- at workspace row ((query row) * q_heads + head) * num_parts +
@@ -593,8 +605,16 @@ __global__ __launch_bounds__(kMergeLanes * kMergeRowsPerWg) void extend_merge_ke
   if (s >= a.num_seqs) return;
   const int q0 = a.query_start[s];
   if (q0 < 0) return;
-  const int n = live_tokens(a, q0, a.query_start[s + 1] - q0);
+  const int n_raw = a.query_start[s + 1] - q0;
+  const int n = live_tokens(a, q0, n_raw);
   if (j >= n) return;
+  // Rows of a query tile whose keys fit the first partition: stored by the
+  // kernel.
+  const int tokens = kExtendCols / (a.q_heads / a.kv_heads);
+  const int L = a.seq_lens[s];
+  const int BS = (int)(a.block_bytes / a.row_bytes);
+  if (tile_key_bound(a, L, L - n_raw, min((j / tokens + 1) * tokens, n), BS) <= a.part_tokens)
+    return;
   const int64_t base = ((int64_t)(q0 + j) * a.q_heads + h) * a.num_parts;
   const float* ml = a.part_ml + 2 * base;
   const float* po = a.part_o + base * kD + 4 * sub;
