@@ -153,6 +153,35 @@ def test_extend_units_of_uneven_query_tiles(S, Hkv, G, new_hi, part):
     compare(out, ref, "bf16")
 
 
+@pytest.mark.parametrize("S", [40, 80])
+def test_extend_split_with_tiles_inside_the_first_partition(S):
+    """A split call in which many query tiles' keys fit the first 64-key
+    partition (those workgroups store their rows and the merge skips them)
+    and the others span two or three partitions, in a batch the workgroups
+    rank (40 sequences) and one they keep in batch order (80); every output
+    row against the oracle."""
+    rng = np.random.default_rng(7700 + S)
+    BS, Hkv, G = 16, 2, 4
+    ctx = rng.integers(0, 120, size=S)
+    new = rng.integers(0, 11, size=S)
+    ctx[rng.integers(0, S, size=S // 4)] = 0            # some tiles end below 64 keys
+    lens = ctx + new
+    kc, vc, table = _pool(rng, lens, BS, Hkv, 128, "bf16", 5)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    T = int(qs[-1])
+    q = _values(rng, (T, Hkv * G, 128), "bf16")
+    log(f"extend split, tiles in the first partition: S={S} T={T}")
+    assert pkv.extend_partition_tokens(to_device(kc, "bf16"), S, T, Hkv * G, int(new.max()),
+                                       int(lens.max()), 64) == 64
+    out = pkv.paged_attn_extend(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
+                                to_device(table, None), to_device(lens.astype(np.int32), None),
+                                to_device(qs, None), 0.09, int(new.max()), int(lens.max()),
+                                part_tokens=64)
+    torch.cuda.synchronize()
+    ref = oracle.extend_attention(q, kc, vc, table, lens, qs, 0.09, "bf16")
+    compare(out, ref, "bf16")
+
+
 @pytest.mark.parametrize("S,ties", [(63, False), (64, False), (65, False), (513, False),
                                     (60, True)])
 def test_extend_many_sequences_in_any_unit_order(S, ties):
