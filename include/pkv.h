@@ -243,7 +243,8 @@ size_t pkv_decode_noalloc_max_workspace(void);
  *                0.  Contents need no initialisation and are left undefined.
  *                It holds each partition's max, sum and normalised output
  *                (all fp32) per query row and head, merged by a second
- *                kernel in a fixed order.
+ *                kernel in a fixed order; rows whose query tile reads no
+ *                key past the first partition are stored directly.
  * Supported: bf16 caches with head_dim 128, block_size 16 or 32, G in
  * {1, 2, 4, 8}; anything else returns PKV_ERR_UNSUPPORTED.
  */
