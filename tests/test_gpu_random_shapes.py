@@ -87,6 +87,42 @@ def test_decode_random_shapes(seed):
     compare(out, ref, dtype)
 
 
+@pytest.mark.parametrize("dtype,Hkv,G,part", [
+    ("bf16", 3, 4, 0),      # one kv head per workgroup, three workgroups per run
+    ("bf16", 6, 4, 64),     # two kv heads per workgroup, three per run
+    ("bf16", 12, 2, 0),     # four kv heads per workgroup, three per run
+    ("bf16", 5, 8, 16),
+    ("f32", 6, 2, 0),
+])
+def test_decode_kv_head_counts_not_a_power_of_two(dtype, Hkv, G, part):
+    """Kv head counts that split into 3 or 5 workgroups per run (the run
+    mapping without the one-group-per-XCD layout of sharing batches), with
+    groups of sequences that share leading blocks; every row against the
+    oracle."""
+    rng = np.random.default_rng(5600 + Hkv * 10 + G)
+    D = 64 if dtype == "f32" else 128
+    BS = 16
+    S = int(rng.integers(30, 70))
+    lens = rng.integers(0, 900, size=S)
+    lens[0] = 0
+    kc, vc, table = _pool(rng, lens, BS, Hkv, D, dtype, 9)
+    gs = 16 // G if dtype == "bf16" else 2
+    for s0 in range(0, S, gs):
+        members = range(s0, min(s0 + gs, S))
+        nb = min(-(-int(lens[s]) // BS) for s in members)
+        J = int(rng.integers(0, nb + 1))
+        for s in members:
+            table[s, :J] = table[s0, :J]
+    q = _values(rng, (S, Hkv * G, D), dtype)
+    log(f"decode kv heads {Hkv}: {dtype} S={S} G={G} part={part}")
+    out = pkv.paged_attn_decode(to_device(q, dtype), to_device(kc, dtype), to_device(vc, dtype),
+                                to_device(table, None), to_device(lens.astype(np.int32), None),
+                                0.1, int(lens.max()), part_tokens=part)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(q, kc, vc, table, lens, 0.1, dtype)
+    compare(out, ref, dtype)
+
+
 @pytest.mark.parametrize("seed", range(32))
 def test_extend_random_shapes(seed):
     rng = np.random.default_rng(6000 + seed)
